@@ -1,0 +1,156 @@
+"""The oracle's whole step: ZeRO equivalence, skip-on-overflow and loss-scale
+bookkeeping, multi-group norm.
+
+* ZeRO equivalence: each rank stepping only its segment, concatenated, equals
+  every rank stepping the whole vector as plain data parallelism does, because
+  the update of one coordinate depends only on that coordinate (ZeRO reading
+  notes, second part §3; DeepSpeed walkthrough §3 "each rank owns one segment").
+* Overflow: inf/NaN anywhere in the group's partition gradients lowers the loss
+  scale and voids the step (DeepSpeed walkthrough §6 step 1).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from workloads import grads16_np, normal_f32_np, to16_bits_np
+
+
+def _group(n, n_d, dt, seed, scale=1.0, wd=0.0, param=None):
+    reps = [grads16_np(n, dt, scale, seed=(seed, r)) for r in range(n_d)]
+    master = normal_f32_np(n, 0.02, (seed, "master"))
+    odt = oracle.F16 if dt == "f16" else oracle.BF16
+    return oracle.Group(replicas=reps, grad_dt=odt, master=master,
+                        m=np.zeros(n, np.float32), v=np.zeros(n, np.float32),
+                        param=param, param_dt=odt, weight_decay=wd)
+
+
+@pytest.mark.parametrize("n_d,psi", [(2, 1001), (3, 10_000), (4, 787_971 // 16), (8, 4099)])
+def test_zero_equivalence(n_d, psi):
+    dt = "f16"
+    steps = 3
+    full_reps = [[grads16_np(psi, dt, 1.0, seed=(k, r)) for r in range(n_d)] for k in range(steps)]
+    master0 = normal_f32_np(psi, 0.02, "m0")
+    # plain data parallelism: the whole vector, averaged over all copies
+    full = oracle.Group(replicas=None, grad_dt=oracle.F16, master=master0.copy(),
+                        m=np.zeros(psi, np.float32), v=np.zeros(psi, np.float32),
+                        param=np.zeros(psi, np.uint16))
+    st_full = oracle.State()
+    full_norms = []
+    for k in range(steps):
+        full.replicas = full_reps[k]
+        oracle.step([full], oracle.Policy(), st_full)
+        full_norms.append(st_full.norm2)
+    # ZeRO: each rank steps its own segment
+    offs, sizes, _ = oracle.partition(psi, n_d)
+    flat_param = np.zeros(psi, np.uint16)
+    master, m, v = np.empty(psi, np.float32), np.empty(psi, np.float32), np.empty(psi, np.float32)
+    rank_norms = np.zeros(steps)
+    for r in range(n_d):
+        o, s = int(offs[r]), int(sizes[r])
+        g = oracle.Group(replicas=None, grad_dt=oracle.F16, master=master0[o:o + s].copy(),
+                         m=np.zeros(s, np.float32), v=np.zeros(s, np.float32),
+                         param=flat_param[o:o + s])
+        st = oracle.State()
+        for k in range(steps):
+            g.replicas = [c[o:o + s] for c in full_reps[k]]
+            oracle.step([g], oracle.Policy(), st)
+            rank_norms[k] += st.norm2
+        master[o:o + s], m[o:o + s], v[o:o + s] = g.master, g.m, g.v
+        assert st.step == steps
+    for a, b in ((master, full.master), (m, full.m), (v, full.v)):
+        np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+    np.testing.assert_array_equal(flat_param, full.param)
+    # the global norm is the sum of the shard-local sums of squares
+    np.testing.assert_allclose(rank_norms, full_norms, rtol=1e-12)
+
+
+def _inject(group, replica, idx, bits):
+    group.replicas[replica] = group.replicas[replica].copy()
+    group.replicas[replica][idx] = bits
+
+
+def test_skip_on_overflow_leaves_everything():
+    n = 3000
+    g = _group(n, 4, "f16", 1, scale=65536.0, param=np.zeros(n, np.uint16))
+    pol = oracle.Policy(skip_on_overflow=True, growth_interval=1000)
+    st = oracle.State(loss_scale=65536.0)
+    oracle.step([g], pol, st)
+    assert st.step == 1 and st.skipped == 0 and st.loss_scale == 65536.0 and st.good_steps == 1
+    snap = [x.copy() for x in (g.master, g.m, g.v, g.param)]
+    g.replicas = [grads16_np(n, "f16", 65536.0, seed=(2, r)) for r in range(4)]
+    _inject(g, 2, n // 2, 0x7C00)
+    oracle.step([g], pol, st)
+    assert st.overflow == 1 and st.skipped == 1
+    assert st.step == 1 and st.loss_scale == 32768.0 and st.good_steps == 0
+    assert not np.isfinite(st.norm2)
+    for a, b in zip((g.master, g.m, g.v, g.param), snap):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_fp16_sum_overflow_and_nan_are_caught():
+    n = 100
+    for bits, dt in ((0x7E00, "f16"), (0xFC00, "f16")):
+        g = _group(n, 2, dt, 3)
+        _inject(g, 0, 99, bits)
+        st = oracle.State()
+        oracle.step([g], oracle.Policy(skip_on_overflow=True), st)
+        assert st.skipped == 1
+    g = _group(n, 2, "bf16", 4)
+    big = to16_bits_np(np.array([3.0e38], np.float32), "bf16")[0]
+    _inject(g, 0, 0, big)
+    _inject(g, 1, 0, big)
+    st = oracle.State()
+    oracle.step([g], oracle.Policy(skip_on_overflow=True), st)
+    assert st.skipped == 1 and st.overflow == 1
+
+
+def test_scale_growth_and_floor():
+    n = 64
+    g = _group(n, 1, "f16", 5, scale=4.0)
+    pol = oracle.Policy(skip_on_overflow=True, growth_interval=2, min_scale=1.0)
+    st = oracle.State(loss_scale=4.0)
+    oracle.step([g], pol, st)
+    assert (st.loss_scale, st.good_steps) == (4.0, 1)
+    oracle.step([g], pol, st)
+    assert (st.loss_scale, st.good_steps, st.step) == (8.0, 0, 2)
+    for expect in (4.0, 2.0, 1.0, 1.0):
+        bad = _group(n, 1, "f16", 6)
+        _inject(bad, 0, 1, 0x7C00)
+        oracle.step([bad], pol, st)
+        assert st.loss_scale == expect and st.step == 2
+
+
+def test_static_scale_applies_even_on_overflow():
+    n = 16
+    g = _group(n, 1, "f16", 7)
+    _inject(g, 0, 3, 0x7C00)
+    st = oracle.State(loss_scale=2.0)
+    oracle.step([g], oracle.Policy(skip_on_overflow=False), st)
+    assert st.step == 1 and st.skipped == 0 and st.loss_scale == 2.0
+    assert not np.isfinite(g.master[3]) and np.isfinite(np.delete(g.master, 3)).all()
+
+
+def test_multi_group_norm_and_shared_skip():
+    a = _group(1000, 1, "bf16", 8, wd=0.1)
+    b = _group(37, 1, "bf16", 9)
+    st = oracle.State()
+    oracle.step([a, b], oracle.Policy(), st)
+    na, _ = oracle.norm_overflow(oracle.average(a.replicas, oracle.BF16), 1.0)
+    nb, _ = oracle.norm_overflow(oracle.average(b.replicas, oracle.BF16), 1.0, na)
+    assert st.norm2 == nb
+    # a non-finite gradient in the small group voids the step for both groups
+    snap = a.master.copy()
+    _inject(b, 0, 36, 0xFF80)
+    oracle.step([a, b], oracle.Policy(skip_on_overflow=True), st)
+    assert st.skipped == 1
+    np.testing.assert_array_equal(a.master, snap)
+
+
+def test_group_hyperparameters_apply_per_group():
+    a = _group(200, 1, "f16", 10, wd=0.1)
+    b = _group(200, 1, "f16", 10, wd=0.0)  # same inputs, no decay
+    oracle.step([a, b], oracle.Policy(), oracle.State())
+    assert not np.array_equal(a.master, b.master)
+    a2 = _group(200, 1, "f16", 10, wd=0.1)
+    oracle.step([a2], oracle.Policy(), oracle.State())
+    np.testing.assert_array_equal(a.master, a2.master)
