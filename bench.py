@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Throughput of the ZeRO-DP partitioned optimizer step on one MI355X.
+
+One step is the whole path for one rank's shard: average the N_d gradient
+copies, overflow flag and gradient norm, fp32 Adam/AdamW on master / m / v,
+16-bit writeback into the flat parameter vector, step bookkeeping. Inputs are
+seeded synthetic tensors already resident in HBM when timing starts.
+
+Prints one JSON line: params updated per second (value), with the achieved
+HBM bandwidth of the step against the bytes model (2*N_d + 26 bytes per
+parameter: the 16-bit copies read once, fp32 master/m/v read and written, the
+16-bit parameter written) and against MI355X's 8 TB/s, and the CPU oracle
+timed on a bounded sample of the same workload on this host.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt2_1.5b]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+DEFAULT_WORKLOAD = "gpt2_1.5b"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "zero_dp_partitioned_amd", "csrc", "kernels.hip")
+
+
+def bytes_per_param(n_d):
+    """Algorithmic HBM bytes of one step per parameter of the shard."""
+    return 2 * n_d + 12 + 12 + 2
+
+
+def kernel_source_hash():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--cpu-sample", type=int, default=1 << 27,
+                   help="elements of the shard the CPU oracle steps once (0: skip)")
+    p.add_argument("--quiet", action="store_true")
+    return p.parse_args()
+
+
+def log(args, *a):
+    if not args.quiet:
+        print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+class Setup:
+    """Device buffers of one workload: per group the fp32 master / m / v shard,
+    the N_d 16-bit gradient copies of the shard (one buffer, 64-element padded
+    stride), and the group's whole 16-bit flat parameter vector."""
+
+    def __init__(self, wl, dev):
+        import torch
+        import zero_dp_partitioned_amd as zdp
+        from workloads import derive_seed, fill_normal_, torch_dtype
+
+        self.wl = wl
+        self.groups = []
+        self.shard = 0
+        gdt, pdt = torch_dtype(wl.grad_dt), torch_dtype(wl.param_dt)
+        for gi, spec in enumerate(wl.groups):
+            psi = sum(spec.numels)
+            segs, _ = zdp.partition(psi, wl.n_d)
+            off, n = segs[wl.rank]
+            master = torch.empty(n, dtype=torch.float32, device=dev)
+            fill_normal_(master, 0.02, derive_seed(wl.key, gi, "master"))
+            flat = torch.empty(psi, dtype=pdt, device=dev)
+            fill_normal_(flat, 0.02, derive_seed(wl.key, gi, "flat"))
+            flat[off:off + n].copy_(master)
+            stride = ((n + 63) // 64) * 64
+            gbuf = torch.empty(max(1, wl.n_d * stride), dtype=gdt, device=dev)
+            reps = [gbuf[r * stride:r * stride + n] for r in range(wl.n_d)]
+            for r, t in enumerate(reps):
+                fill_normal_(t, 1e-3, derive_seed(wl.key, gi, "grad", 0, r), scale=wl.loss_scale)
+            self.groups.append(zdp.Group(
+                master=master, exp_avg=torch.zeros_like(master), exp_avg_sq=torch.zeros_like(master),
+                replicas=reps, flat_param=flat, param_offset=off, lr=wl.lr, beta1=wl.beta1,
+                beta2=wl.beta2, eps=wl.eps, weight_decay=spec.weight_decay))
+            self.shard += n
+        self.ws = zdp.new_workspace(len(self.groups))
+        self.state = zdp.new_state(wl.loss_scale)
+        self.scaler = zdp.scaler(True) if wl.dynamic_loss_scale else None
+        if wl.dynamic_loss_scale:
+            self.avg = [torch.empty_like(g.master) for g in self.groups]
+
+    def step(self):
+        import zero_dp_partitioned_amd as zdp
+        if self.scaler is None:
+            zdp.adam_step(self.groups, self.ws, self.state)
+            return
+        # dynamic loss scale: average pass, norm / overflow verdict, checked update
+        for gi, g in enumerate(self.groups):
+            zdp.reduce_grad_segment(g.replicas, self.avg[gi], self.ws, gi, self.state)
+        zdp.grad_norm_overflow(None, self.ws, len(self.groups), self.state, self.scaler)
+        reps = [g.replicas for g in self.groups]
+        for gi, g in enumerate(self.groups):
+            g.replicas, g.avg = None, self.avg[gi]
+        try:
+            zdp.adam_step(self.groups, self.ws, self.state, self.scaler)
+        finally:
+            for gi, g in enumerate(self.groups):
+                g.replicas, g.avg = reps[gi], None
+
+
+def cpu_baseline(setup, sample, args):
+    """The CPU oracle, single-threaded, on the first `sample` elements of the
+    first group's shard, for one step."""
+    import numpy as np
+    import torch
+
+    import oracle  # CPU oracle: used here only for the reported baseline
+
+    wl = setup.wl
+    g = setup.groups[0]
+    k = min(sample, g.master.numel())
+    odt = oracle.F16 if wl.grad_dt == "f16" else oracle.BF16
+    reps = [r[:k].cpu().view(torch.int16).numpy().view(np.uint16).copy() for r in g.replicas]
+    og = oracle.Group(replicas=reps, grad_dt=odt, master=g.master[:k].cpu().numpy().copy(),
+                      m=np.zeros(k, np.float32), v=np.zeros(k, np.float32),
+                      param=np.zeros(k, np.uint16), param_dt=odt, lr=wl.lr, beta1=wl.beta1,
+                      beta2=wl.beta2, eps=wl.eps, weight_decay=wl.groups[0].weight_decay)
+    st = oracle.State(loss_scale=wl.loss_scale)
+    oracle.lib()
+    log(args, f"cpu oracle: one step over {k} elements on 1 thread")
+    t0 = time.perf_counter()
+    oracle.step([og], oracle.Policy(skip_on_overflow=wl.dynamic_loss_scale), st)
+    dt = time.perf_counter() - t0
+    return {"value": k / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {k} elements of the {wl.key} shard (N_d={wl.n_d}), one step, "
+                      f"single-threaded scalar C oracle, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs the single-rank step on one GPU; --gpus {args.gpus} is not "
+              f"supported (no collectives, no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import zero_dp_partitioned_amd as zdp
+    from workloads import WORKLOADS
+
+    zdp.load()
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = WORKLOADS[args.workload]
+    log(args, f"workload {wl.key}: {wl.title}")
+    setup = Setup(wl, dev)
+    S = setup.shard
+    bpp = bytes_per_param(wl.n_d)
+    log(args, f"shard {S} params, {len(setup.groups)} group(s), {bpp} B/param, "
+              f"{S * bpp / 1e9:.2f} GB per step")
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        setup.step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        starts[k].record(stream)
+        setup.step()
+        ends[k].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    ev_mean = sum(ev_ms) / len(ev_ms)
+    ms_per_step = wall * 1e3 / args.steps
+    st = zdp.read_state(setup.state)
+    log(args, f"steps {args.steps}: wall {ms_per_step:.3f} ms/step, events mean {ev_mean:.3f} "
+              f"median {ev_ms[len(ev_ms) // 2]:.3f} min {ev_ms[0]:.3f} ms; state step {st['step']} "
+              f"norm {st['grad_norm']:.6g} scale {st['loss_scale']}")
+    value = S / (ms_per_step / 1e3)
+    algo_bytes = S * bpp
+    achieved = algo_bytes / (ev_mean / 1e3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE)).get(wl.key)
+        if rec and rec.get("kernel_source") == kernel_source_hash():
+            traffic = rec.get("bytes_per_launch")
+    cpu = None
+    if args.cpu_sample > 0:
+        cpu = cpu_baseline(setup, args.cpu_sample, args)
+    out = {
+        "metric": "params updated/sec and achieved HBM GB/s (% peak) per sharded Adam step",
+        "value": value,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.key, "shard_params": S, "n_d": wl.n_d, "rank": wl.rank,
+                   "groups": len(setup.groups), "grad_dtype": wl.grad_dt, "param_dtype": wl.param_dt,
+                   "loss_scale": wl.loss_scale, "dynamic_loss_scale": wl.dynamic_loss_scale,
+                   "bytes_per_param": bpp},
+        "gbps": achieved,
+        "pct_peak": 100.0 * achieved / PEAK_HBM_GBPS,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+                     "kernel": "adam_kernel (fused step) + 1-block finalize, HIP events per step",
+                     "kernel_ms": ev_mean, "algorithmic_bytes": algo_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

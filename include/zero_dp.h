@@ -1,0 +1,236 @@
+/*
+ * zero_dp.h -- C ABI of the ZeRO-DP partitioned optimizer step for AMD MI355X
+ * (gfx950). One rank's shard, on one GPU.
+ *
+ * The step follows the pages on ZeRO:
+ *   - "DeepSpeed ZeRO stage 1/2" walkthrough ("01 · ZeRO 的显存数学与 Stage 1/2"):
+ *     §3 (flatten a parameter group into one vector, split it into N_d
+ *     segments, each rank owns one), §4 ② (base = numel / N_d, remainder to the
+ *     first ranks), §4 ④ / §7 (a tensor may straddle two segments; alignment
+ *     padding), §6 (step: overflow check and skip, global norm, unscale, Adam on
+ *     the shard, copy the fp32 shard back into the 16-bit flat vector).
+ *   - "ZeRO: Memory Optimizations Toward Training Trillion Parameter Models"
+ *     reading notes, second part §3 (per-coordinate Adam update) and §4 (the
+ *     averaged shard is (1/N_d) * sum over ranks of that shard).
+ *   - ZeRO paper translation, §3.1 (fp16/bf16 params and grads, fp32 master,
+ *     momentum and variance).
+ *
+ * Conventions for every call:
+ *   - All device buffers are owned by the caller. The library never allocates
+ *     or frees device memory and keeps no state between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work
+ *     is enqueued asynchronously, in stream order; no call synchronises the
+ *     host. Scalar results (norm, overflow flag, loss scale, step count) stay in
+ *     the device-resident zero_step_state.
+ *   - Arguments are checked on the host before anything is enqueued: a
+ *     non-zero return means nothing was launched, and zero_last_error() gives a
+ *     thread-local message. Numerical overflow is not an error; it is a flag.
+ *     A device fault surfaces at the caller's next synchronisation.
+ *   - Calls on different streams with disjoint buffers may run concurrently.
+ *     Calls that share a workspace or a state must be ordered by the caller.
+ *   - Element counts and offsets are int64 (offsets above 2^32 are normal).
+ */
+#ifndef ZERO_DP_H
+#define ZERO_DP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ------------------------------------------------------ */
+#define ZERO_OK 0
+#define ZERO_ERR_INVALID_ARG (-1) /* null pointer, bad count, dtype, rank ... */
+#define ZERO_ERR_ALIGNMENT (-2)   /* fp32 pointer not 4-byte, 16-bit not 2-byte aligned */
+#define ZERO_ERR_WORKSPACE (-3)   /* workspace missing or group index out of range */
+#define ZERO_ERR_HIP (-4)         /* a HIP runtime call or launch failed */
+#define ZERO_ERR_UNSUPPORTED (-5) /* device is not gfx950, or a size limit below */
+
+/* ---- limits ------------------------------------------------------------ */
+#define ZERO_MAX_GROUPS 8       /* parameter groups per step / per state */
+#define ZERO_MAX_REPLICAS 4096  /* N_d */
+
+/* ---- dtypes (values are part of the ABI) -------------------------------- */
+#define ZERO_DT_F16 1  /* IEEE binary16 */
+#define ZERO_DT_BF16 2 /* bfloat16 */
+
+/* One rank's segment of a flat vector: elements [offset, offset + size). */
+typedef struct {
+  int64_t offset;
+  int64_t size;
+} zero_segment;
+
+/* The part of tensor `tensor` that lies inside a rank's segment:
+ * shard[shard_begin + i] is tensor[tensor_begin + i] for i < length. */
+typedef struct {
+  int32_t tensor;
+  int32_t reserved;
+  int64_t shard_begin;
+  int64_t tensor_begin;
+  int64_t length;
+} zero_tensor_slice;
+
+/* Optimizer and loss-scale state of one rank, resident in device memory.
+ * Allocate sizeof(zero_step_state) bytes (8-byte aligned) and fill it with
+ * zero_state_init(). The kernels read and write it; the host reads it after
+ * synchronising (for example to log the norm or the loss scale). */
+typedef struct {
+  double beta1_pow[ZERO_MAX_GROUPS]; /* beta1^t per group (t = applied steps), by
+                                        successive fp64 multiplication       */
+  double beta2_pow[ZERO_MAX_GROUPS]; /* beta2^t per group                    */
+  double grad_norm_sq;  /* last step: sum of squares of the unscaled averaged
+                           gradient over all groups, in fp64                  */
+  float grad_norm;      /* sqrt(grad_norm_sq) rounded to fp32                  */
+  float loss_scale;     /* S: stored gradients are the true ones times S       */
+  int64_t step;         /* applied steps t                                     */
+  int32_t overflow;     /* last step: 1 if any averaged gradient was inf/NaN   */
+  int32_t skipped;      /* last step: 1 if it was voided by the overflow check */
+  int32_t good_steps;   /* applied steps since the last loss-scale change      */
+  int32_t reserved;
+} zero_step_state;
+
+/* Loss-scale policy. skip_on_overflow = 0: static scale, every step applies
+ * (an inf/NaN gradient then propagates into the state). skip_on_overflow = 1:
+ * dynamic scale: a step whose averaged gradient holds inf/NaN changes nothing
+ * but the scale (S <- max(S * backoff, min_scale)); after growth_interval
+ * applied steps in a row, S <- S * growth (growth_interval 0 = never). */
+typedef struct {
+  int32_t skip_on_overflow;
+  int32_t growth_interval;
+  double backoff;
+  double growth;
+  double min_scale;
+} zero_scaler;
+
+/* One parameter group's shard for zero_adam_step().
+ * Gradient source, exactly one of:
+ *   replicas: host array of n_d device pointers, each to n elements of
+ *             grad_dt: the N_d gradient copies of this rank's segment. Their
+ *             average is formed in the kernel (fused mode), or
+ *   avg:      device fp32 [n] average written by zero_reduce_grad_segment().
+ * State: master, exp_avg (m), exp_avg_sq (v): device fp32 [n], updated in place.
+ * Writeback: flat_param (device, param_dt elements) receives the updated master
+ *   rounded to 16 bits at elements [param_offset, param_offset + n); NULL skips
+ *   it. Any 2-byte alignment of flat_param + param_offset is accepted.
+ * Hyperparameters: lr, beta1, beta2, eps; weight_decay != 0 applies decoupled
+ *   (AdamW) decay master *= (1 - lr * weight_decay) before the Adam update. */
+typedef struct {
+  int64_t n;
+  const void* const* replicas;
+  int32_t n_d;
+  int32_t grad_dt;
+  const float* avg;
+  float* master;
+  float* exp_avg;
+  float* exp_avg_sq;
+  void* flat_param;
+  int64_t param_offset;
+  int32_t param_dt;
+  int32_t reserved;
+  double lr, beta1, beta2, eps, weight_decay;
+} zero_group;
+
+/* ---- host-only calls ---------------------------------------------------- */
+
+/* Partition a flat vector of `numel` elements over n_d ranks [DeepSpeed
+ * walkthrough §4 ②]: after optional padding of numel up to a multiple of
+ * align_elems (1 = none) [§4 ①, §7], base = padded / n_d, rem = padded % n_d,
+ * rank r gets base + (r < rem) elements starting at r * base + min(r, rem).
+ * segs: host array of n_d entries (written). padded_numel: may be NULL.
+ * Errors: INVALID_ARG for numel < 0, n_d < 1, align_elems < 1, NULL segs,
+ * int64 overflow. */
+int zero_partition(int64_t numel, int32_t n_d, int64_t align_elems,
+                   zero_segment* segs, int64_t* padded_numel);
+
+/* The tensor slices inside rank `rank`'s segment when n_tensors tensors of
+ * numels[i] elements are laid end to end into one flat vector and partitioned
+ * as zero_partition() does [DeepSpeed walkthrough §3 ①, §4 ④]. Writes up to
+ * `cap` entries of `out` in tensor order and their count to *n_out.
+ * Errors: INVALID_ARG (bad counts, rank out of range, cap too small). */
+int zero_partition_tensors(const int64_t* numels, int32_t n_tensors, int32_t n_d,
+                           int32_t rank, int64_t align_elems, zero_tensor_slice* out,
+                           int32_t cap, int32_t* n_out);
+
+/* Bytes of device workspace the step calls need for n_groups groups (norm and
+ * overflow partials). Constant in the shard size. 0 if n_groups is out of
+ * range. The workspace must be 256-byte aligned; its contents need no
+ * initialisation. Every call that takes a workspace also takes its size and
+ * returns ZERO_ERR_WORKSPACE if it is smaller than the slots the call uses
+ * need (slot g needs zero_workspace_bytes(g + 1)). */
+size_t zero_workspace_bytes(int32_t n_groups);
+
+/* Thread-local text of the last error returned on this thread. */
+const char* zero_last_error(void);
+
+/* ---- device calls -------------------------------------------------------- */
+
+/* Initialise a device zero_step_state: beta powers 1, step 0, loss scale
+ * `loss_scale` (> 0), flags and norm 0. */
+int zero_state_init(zero_step_state* state, float loss_scale, void* stream);
+
+/* Average this rank's segment over its N_d gradient copies [reading notes,
+ * second part §4: avg = (1/N_d) * sum_r g_r]: for each j < n,
+ *   acc = 0 (fp32); acc += float(replicas[r][j]) for r = 0 .. n_d-1 in order;
+ *   avg_out[j] = acc / n_d.
+ * avg_out keeps the loss scale (it is not unscaled). The same pass writes the
+ * overflow flag and sum-of-squares partials of the unscaled gradient
+ * avg_out[j] * (1 / state->loss_scale) into workspace slot `group`, for
+ * zero_grad_norm_overflow(). replicas: host array of n_d device pointers.
+ * Errors: INVALID_ARG, ALIGNMENT, WORKSPACE, UNSUPPORTED (n_d too large). */
+int zero_reduce_grad_segment(const void* const* replicas, int32_t n_d, int32_t grad_dt,
+                             int64_t n, float* avg_out, void* workspace, size_t workspace_bytes,
+                             int32_t group, const zero_step_state* state, void* stream);
+
+/* Overflow check and gradient norm of one step [DeepSpeed walkthrough §6
+ * steps 1-2]. If `grads` is not NULL, first scan grads[g] (device pointer to
+ * counts[g] elements of grad_dt, a single gradient copy, N_d = 1) into
+ * workspace slot g for each g < n_groups with grads[g] != NULL. Then combine
+ * the partials of slots 0 .. n_groups-1 in a fixed order into
+ * state->grad_norm_sq / grad_norm (the norm of the unscaled gradient over all
+ * groups) and state->overflow, and set state->skipped = overflow &&
+ * scaler->skip_on_overflow (scaler may be NULL: no skip). Does not advance
+ * the step. `grads` and `counts` are host arrays.
+ * Errors: INVALID_ARG, ALIGNMENT, WORKSPACE. */
+int zero_grad_norm_overflow(const void* const* grads, const int64_t* counts, int32_t grad_dt,
+                            int32_t n_groups, void* workspace, size_t workspace_bytes,
+                            const zero_scaler* scaler, zero_step_state* state, void* stream);
+
+/* One Adam/AdamW step over n_groups groups of this rank's shard [reading
+ * notes, second part §3; DeepSpeed walkthrough §6 steps 3-5]. With applied
+ * step t = state->step + 1, per group b1 = fp32(1 - beta1^t),
+ * b2 = fp32(1 - beta2^t), and per element, every operation in fp32
+ * round-to-nearest-even, no fused multiply-add:
+ *   g = avg * fp32(1 / S);  theta = master;  if wd: theta *= fp32(1 - lr*wd)
+ *   m = beta1*m + fp32(1-beta1)*g;   v = beta2*v + fp32(1-beta2)*(g*g)
+ *   theta -= lr * ((m / b1) / (sqrt(v / b2) + eps))
+ *   master = theta;  flat_param[param_offset + j] = RNE16(theta)
+ * Pipelines, chosen by the scaler:
+ *   - static scale (scaler NULL or skip_on_overflow 0), "fused": one pass per
+ *     group reads the gradient source, averages, unscales, updates and writes
+ *     back, and emits norm/overflow partials; a final one-block kernel forms
+ *     the norm and the flag and advances the step. No
+ *     zero_grad_norm_overflow() call is needed.
+ *   - dynamic scale (skip_on_overflow 1), "checked": the caller has already run
+ *     zero_grad_norm_overflow() on this step's gradients; if it set
+ *     state->skipped, nothing but the loss scale changes; otherwise the update
+ *     is applied and the step advances. Scale backoff/growth happen here.
+ * `groups` is a host array; group g uses workspace slot g and the beta powers
+ * state->beta*_pow[g].
+ * Errors: INVALID_ARG, ALIGNMENT, WORKSPACE, UNSUPPORTED. */
+int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_scaler* scaler,
+                   void* workspace, size_t workspace_bytes, zero_step_state* state, void* stream);
+
+/* Copy an fp32 master shard into the 16-bit flat vector [DeepSpeed
+ * walkthrough §6 step 5]: flat_param[offset + j] = RNE16(master[j]) for j < n
+ * (NaN becomes the canonical quiet NaN). Used at initialisation and to restore
+ * parameters from the master. Errors: INVALID_ARG, ALIGNMENT. */
+int zero_cast_writeback(const float* master, int64_t n, void* flat_param, int64_t offset,
+                        int32_t param_dt, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO_DP_H */

@@ -9,3 +9,22 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long CPU test")
+
+
+def pytest_collection_modifyitems(config, items):
+    """GPU tests need a GPU. Where there is none they are skipped; where there
+    is one they run, and a missing library makes them fail, not skip."""
+    gpu_items = [it for it in items if "gpu" in it.keywords]
+    if not gpu_items:
+        return
+    try:
+        import torch
+        have_gpu = torch.cuda.is_available()
+    except Exception:  # pragma: no cover
+        have_gpu = False
+    if have_gpu:
+        return
+    import pytest
+    skip = pytest.mark.skip(reason="no GPU visible")
+    for it in gpu_items:
+        it.add_marker(skip)

@@ -1,0 +1,338 @@
+"""GPU parity: every C-ABI call against the CPU oracle, element by element, on
+seeded inputs that span several tiles, ragged tails, both 16-bit dtypes, N_d
+from 1 to 100, every alignment class of the parameter slice, and the edge
+cases of the method (empty shard, overflow with and without skip, loss-scale
+backoff and growth, several groups).
+
+Bar: fp32 master / m / v and the 16-bit parameters bit-identical to the
+oracle (NaN compared as NaN), the overflow flag, step count, skip verdict and
+loss scale exact, the fp64 gradient norm within 1e-10 relative (the two sides
+sum in different orders)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import zero_dp_partitioned_amd as zdp
+from workloads import grads16_np, normal_f32_np, to16_bits_np
+
+from _gpu_helpers import (DEV, ORACLE_DT, TORCH16, assert_bits_equal, assert_u16_equal, carve,
+                          down16, down32, up16, up32)
+
+pytestmark = pytest.mark.gpu
+
+NORM_RTOL = 1e-10
+POS_INF = {"f16": 0x7C00, "bf16": 0x7F80}
+NEG_NAN = {"f16": 0xFE00, "bf16": 0xFFC0}
+
+
+def _replicas_on_device(reps, dt, layout):
+    n = reps[0].size
+    if layout == "table":
+        return [up16(r, dt) for r in reps]
+    # one buffer, copies equally spaced: padded to 64 elements ("strided") or
+    # packed back to back so that most copies start unaligned ("packed")
+    stride = ((n + 63) // 64) * 64 if layout == "strided" else n
+    buf = torch.empty(max(1, stride * len(reps)), dtype=TORCH16[dt], device=DEV)
+    out = []
+    for r, bits in enumerate(reps):
+        view = buf[r * stride:r * stride + n]
+        view.copy_(up16(bits, dt))
+        out.append(view)
+    return out
+
+
+def _compare_group(tag, master, m, v, og):
+    got_master = down32(master)
+    nan = np.isnan(og.master)
+    assert (np.isnan(got_master) == nan).all(), f"{tag}: NaN positions of master differ"
+    assert_bits_equal(np.where(nan, 0, got_master), np.where(nan, 0, og.master), f"{tag} master")
+    assert_bits_equal(down32(m), og.m, f"{tag} exp_avg")
+    assert_bits_equal(down32(v), og.v, f"{tag} exp_avg_sq")
+
+
+def _compare_state(tag, st, ost):
+    s = zdp.read_state(st)
+    assert s["step"] == ost.step, tag
+    assert s["overflow"] == ost.overflow, tag
+    assert s["skipped"] == ost.skipped, tag
+    assert s["loss_scale"] == np.float32(ost.loss_scale), tag
+    assert s["good_steps"] == ost.good_steps, tag
+    if np.isfinite(ost.norm2):
+        assert abs(s["grad_norm_sq"] - ost.norm2) <= NORM_RTOL * ost.norm2, (tag, s["grad_norm_sq"], ost.norm2)
+        assert s["grad_norm"] == pytest.approx(np.sqrt(ost.norm2), rel=1e-6)
+    else:
+        assert not np.isfinite(s["grad_norm_sq"]), tag
+    return s
+
+
+def run_fused(n, n_d, dt, steps=3, param_off=0, misalign=0, layout="table", wd=0.0, loss_scale=1.0,
+              seed=0, inject=None):
+    """Fused pipeline for `steps` steps next to the oracle; checks every step."""
+    tag = f"n={n} n_d={n_d} {dt} off={param_off} mis={misalign} {layout} wd={wd}"
+    print(f"[case] {tag}", flush=True)
+    odt = ORACLE_DT[dt]
+    master0 = normal_f32_np(n, 0.02, (seed, "master"))
+    flat0 = to16_bits_np(normal_f32_np(param_off + n + 5, 0.02, (seed, "flat")), dt)
+    master = carve(n + 8, misalign, n, torch.float32)
+    master.copy_(up32(master0))
+    m = carve(n + 8, misalign, n, torch.float32).zero_()
+    v = carve(n + 8, misalign, n, torch.float32).zero_()
+    flat = up16(flat0, dt)
+    ws = zdp.new_workspace(1)
+    st = zdp.new_state(loss_scale)
+    og = oracle.Group(replicas=None, grad_dt=odt, master=master0.copy(), m=np.zeros(n, np.float32),
+                      v=np.zeros(n, np.float32), param=flat0[param_off:param_off + n].copy(),
+                      param_dt=odt, weight_decay=wd)
+    ost = oracle.State(loss_scale=loss_scale)
+    for k in range(steps):
+        reps = [grads16_np(n, dt, loss_scale, (seed, "g", k, r)) for r in range(n_d)]
+        if inject is not None and inject[0] == k:
+            reps[inject[1]] = reps[inject[1]].copy()
+            reps[inject[1]][inject[2]] = inject[3]
+        dreps = _replicas_on_device(reps, dt, layout)
+        zdp.adam_step([zdp.Group(master, m, v, replicas=dreps, flat_param=flat, param_offset=param_off,
+                                 weight_decay=wd)], ws, st)
+        og.replicas = reps
+        oracle.step([og], oracle.Policy(), ost)
+        torch.cuda.synchronize()
+        _compare_group(f"{tag} step {k + 1}", master, m, v, og)
+        _compare_state(f"{tag} step {k + 1}", st, ost)
+    got_flat = down16(flat)
+    assert_u16_equal(got_flat[param_off:param_off + n], og.param, f"{tag} param slice")
+    outside = np.r_[0:param_off, param_off + n:flat0.size]
+    assert_u16_equal(got_flat[outside], flat0[outside], f"{tag} param outside the slice")
+
+
+FUSED_CASES = [
+    # (n, n_d, dt, param_off, misalign, layout)
+    (1, 1, "f16", 0, 0, "table"),
+    (7, 2, "bf16", 3, 0, "table"),
+    (8, 4, "f16", 8, 0, "table"),
+    (9, 3, "bf16", 1, 0, "table"),
+    (255, 8, "f16", 2, 0, "table"),
+    (2048, 1, "bf16", 0, 0, "table"),
+    (2049, 4, "f16", 4, 0, "table"),
+    (10_007, 7, "f16", 6, 0, "table"),
+    (100_003, 1, "bf16", 0, 0, "table"),
+    (100_003, 2, "f16", 5, 0, "table"),
+    (196_993, 4, "f16", 196_993, 0, "table"),   # the tiny workload's rank-1 slice (odd offset)
+    (65_536, 64, "f16", 4, 0, "table"),
+    (65_541, 64, "bf16", 12, 0, "strided"),
+    (30_001, 65, "f16", 0, 0, "strided"),
+    (30_001, 100, "bf16", 2, 0, "strided"),
+    (50_000, 8, "f16", 0, 0, "packed"),         # unaligned copies: element path
+    (50_001, 2, "bf16", 0, 1, "table"),         # unaligned fp32 state: element path
+    (4_500_001, 1, "bf16", 0, 0, "table"),      # more than one grid-stride round
+    (4_500_013, 3, "f16", 7, 0, "table"),
+]
+
+
+@pytest.mark.parametrize("n,n_d,dt,param_off,misalign,layout", FUSED_CASES)
+def test_fused_step_matches_oracle(n, n_d, dt, param_off, misalign, layout):
+    run_fused(n, n_d, dt, steps=3, param_off=param_off, misalign=misalign, layout=layout)
+
+
+def test_fused_empty_shard():
+    run_fused(0, 4, "f16", steps=2, param_off=3)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_fused_adamw_and_loss_scale(dt):
+    run_fused(20_001, 2, dt, steps=4, param_off=1, wd=0.1, loss_scale=65536.0, seed=3)
+
+
+def test_fused_ten_steps():
+    run_fused(40_000, 4, "bf16", steps=10, param_off=0, seed=4)
+
+
+def test_fused_static_scale_overflow_propagates():
+    # no skip policy: the inf enters the update exactly as in the oracle
+    run_fused(3000, 2, "f16", steps=3, inject=(1, 1, 1234, 0x7C00), seed=5)
+    run_fused(3000, 1, "bf16", steps=2, inject=(0, 0, 2999, 0x7FC0), seed=6)
+
+
+def test_replica_table_beyond_64_must_be_strided():
+    n, n_d = 100, 65
+    buf = torch.zeros(n_d * 128, dtype=torch.float16, device=DEV)
+    views = [buf[r * 128:r * 128 + n] for r in range(n_d)]
+    views[1], views[2] = views[2], views[1]   # not equally spaced any more
+    t = torch.zeros(n, dtype=torch.float32, device=DEV)
+    with pytest.raises(zdp.ZeroError) as e:
+        zdp.adam_step([zdp.Group(t, t.clone(), t.clone(), replicas=views)], zdp.new_workspace(1),
+                      zdp.new_state())
+    assert e.value.code == zdp.ERR_UNSUPPORTED
+
+
+# --------------------------------------------------------------------------
+# checked pipeline: average pass, norm/flag, then the update (skip on overflow)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,n_d,dt,use_avg", [(50_001, 8, "f16", True), (4099, 3, "bf16", True),
+                                              (4099, 2, "f16", False), (7, 5, "f16", True)])
+def test_checked_pipeline_skip_and_scale(n, n_d, dt, use_avg):
+    tag = f"checked n={n} n_d={n_d} {dt} avg={use_avg}"
+    print(f"[case] {tag}", flush=True)
+    odt = ORACLE_DT[dt]
+    pol = oracle.Policy(skip_on_overflow=True, growth_interval=2)
+    sc = zdp.scaler(True, growth_interval=2)
+    master0 = normal_f32_np(n, 0.02, (7, "master"))
+    flat0 = to16_bits_np(normal_f32_np(n + 11, 0.02, (7, "flat")), dt)
+    off = 11
+    master, m, v = up32(master0), torch.zeros(n, device=DEV), torch.zeros(n, device=DEV)
+    avg = torch.empty(n, dtype=torch.float32, device=DEV)
+    flat = up16(flat0, dt)
+    ws, st = zdp.new_workspace(1), zdp.new_state(65536.0)
+    og = oracle.Group(replicas=None, grad_dt=odt, master=master0.copy(), m=np.zeros(n, np.float32),
+                      v=np.zeros(n, np.float32), param=flat0[off:off + n].copy(), param_dt=odt)
+    ost = oracle.State(loss_scale=65536.0)
+    for k in range(7):
+        reps = [grads16_np(n, dt, ost.loss_scale, (7, "g", k, r)) for r in range(n_d)]
+        if k in (2, 3):   # two overflowing calls in a row: the scale halves twice
+            reps[-1] = reps[-1].copy()
+            reps[-1][n // 2] = POS_INF[dt] if k == 2 else NEG_NAN[dt]
+        dreps = [up16(r, dt) for r in reps]
+        zdp.reduce_grad_segment(dreps, avg, ws, 0, st)
+        zdp.grad_norm_overflow(None, ws, 1, st, sc)
+        grp = zdp.Group(master, m, v, avg=avg if use_avg else None, replicas=None if use_avg else dreps,
+                        flat_param=flat, param_offset=off)
+        zdp.adam_step([grp], ws, st, sc)
+        og.replicas = reps
+        oracle.step([og], pol, ost)
+        torch.cuda.synchronize()
+        _compare_group(f"{tag} call {k + 1}", master, m, v, og)
+        _compare_state(f"{tag} call {k + 1}", st, ost)
+        if k == 1:
+            np.testing.assert_array_equal(down32(avg), oracle.average(reps, odt))
+    assert ost.step == 5
+    assert_u16_equal(down16(flat)[off:off + n], og.param, tag + " param")
+
+
+def test_checked_single_copy_prepass_two_groups():
+    """N_d = 1, two groups, dynamic scale: the norm pass scans the gradients
+    directly, then the update re-reads them."""
+    dt = "bf16"
+    odt = ORACLE_DT[dt]
+    sizes, wds = (30_011, 513), (0.1, 0.0)
+    pol = oracle.Policy(skip_on_overflow=True, growth_interval=1000)
+    sc = zdp.scaler(True)
+    dev_groups, ogs, flats = [], [], []
+    for i, (n, wd) in enumerate(zip(sizes, wds)):
+        master0 = normal_f32_np(n, 0.02, (8, i, "master"))
+        flat0 = to16_bits_np(master0, dt)
+        flats.append(up16(flat0, dt))
+        dev_groups.append(zdp.Group(up32(master0), torch.zeros(n, device=DEV), torch.zeros(n, device=DEV),
+                                    flat_param=flats[-1], weight_decay=wd))
+        ogs.append(oracle.Group(replicas=None, grad_dt=odt, master=master0.copy(), m=np.zeros(n, np.float32),
+                                v=np.zeros(n, np.float32), param=flat0.copy(), param_dt=odt, weight_decay=wd))
+    ws, st = zdp.new_workspace(2), zdp.new_state(1024.0)
+    ost = oracle.State(loss_scale=1024.0)
+    for k in range(4):
+        grads = [grads16_np(n, dt, ost.loss_scale, (8, "g", k, i)) for i, n in enumerate(sizes)]
+        if k == 1:
+            grads[1] = grads[1].copy()
+            grads[1][0] = 0xFF80   # -inf in the small group voids the whole step
+        dg = [up16(g, dt) for g in grads]
+        zdp.grad_norm_overflow(dg, ws, 2, st, sc)
+        for G, d in zip(dev_groups, dg):
+            G.replicas = [d]
+        zdp.adam_step(dev_groups, ws, st, sc)
+        for og, g in zip(ogs, grads):
+            og.replicas = [g]
+        oracle.step(ogs, pol, ost)
+        torch.cuda.synchronize()
+        for i, (G, og) in enumerate(zip(dev_groups, ogs)):
+            _compare_group(f"group {i} call {k + 1}", G.master, G.exp_avg, G.exp_avg_sq, og)
+            assert_u16_equal(down16(flats[i]), og.param, f"group {i} param")
+        _compare_state(f"call {k + 1}", st, ost)
+    assert ost.step == 3 and ost.loss_scale == 512.0
+
+
+def test_fused_two_groups_adamw():
+    dt = "bf16"
+    odt = ORACLE_DT[dt]
+    sizes, wds = (123_457, 777), (0.1, 0.0)
+    dev_groups, ogs, flats = [], [], []
+    for i, (n, wd) in enumerate(zip(sizes, wds)):
+        master0 = normal_f32_np(n, 0.02, (9, i))
+        flat0 = to16_bits_np(master0, dt)
+        flats.append(up16(flat0, dt))
+        dev_groups.append(zdp.Group(up32(master0), torch.zeros(n, device=DEV), torch.zeros(n, device=DEV),
+                                    flat_param=flats[-1], weight_decay=wd))
+        ogs.append(oracle.Group(replicas=None, grad_dt=odt, master=master0.copy(), m=np.zeros(n, np.float32),
+                                v=np.zeros(n, np.float32), param=flat0.copy(), param_dt=odt, weight_decay=wd))
+    ws, st = zdp.new_workspace(2), zdp.new_state(1.0)
+    ost = oracle.State()
+    for k in range(3):
+        grads = [grads16_np(n, dt, 1.0, (9, "g", k, i)) for i, n in enumerate(sizes)]
+        for G, g in zip(dev_groups, grads):
+            G.replicas = [up16(g, dt)]
+        zdp.adam_step(dev_groups, ws, st)
+        for og, g in zip(ogs, grads):
+            og.replicas = [g]
+        oracle.step(ogs, oracle.Policy(), ost)
+        torch.cuda.synchronize()
+        for i, (G, og) in enumerate(zip(dev_groups, ogs)):
+            _compare_group(f"group {i} step {k + 1}", G.master, G.exp_avg, G.exp_avg_sq, og)
+            assert_u16_equal(down16(flats[i]), og.param, f"group {i} param")
+        s = _compare_state(f"step {k + 1}", st, ost)
+        want_pow = 1.0
+        for _ in range(k + 1):
+            want_pow = want_pow * 0.9
+        assert s["beta1_pow"][0] == s["beta1_pow"][1] == want_pow
+
+
+# --------------------------------------------------------------------------
+# standalone calls
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("off", [0, 1, 2, 4, 8, 13])
+def test_cast_writeback(dt, off):
+    rng = np.random.Generator(np.random.PCG64(10 + off))
+    n = 20_003
+    x = (rng.standard_normal(n) * 10.0 ** rng.uniform(-10, 6, n)).astype(np.float32)
+    x[:12] = [np.nan, -np.nan, np.inf, -np.inf, 0.0, -0.0, 65504.0, 65520.0, 3.4e38, 1e-40, -1e-45, 2.0 ** -24]
+    flat0 = np.arange(n + off + 3, dtype=np.uint16)
+    flat = up16(flat0, dt)
+    zdp.cast_writeback(up32(x), flat, off)
+    got = down16(flat)
+    assert_u16_equal(got[off:off + n], oracle.encode16(x, ORACLE_DT[dt]), f"cast {dt} off={off}")
+    assert_u16_equal(got[:off], flat0[:off], "before")
+    assert_u16_equal(got[off + n:], flat0[off + n:], "after")
+
+
+@pytest.mark.parametrize("n_d,dt,layout", [(1, "bf16", "table"), (4, "f16", "table"), (64, "f16", "strided"),
+                                           (3, "bf16", "packed"), (100, "f16", "strided")])
+def test_reduce_grad_segment(n_d, dt, layout):
+    n = 70_001
+    reps = [grads16_np(n, dt, 1.0, (11, r)) for r in range(n_d)]
+    reps[0] = reps[0].copy()
+    reps[0][5] = 0x8000   # -0
+    avg = torch.empty(n, dtype=torch.float32, device=DEV)
+    ws, st = zdp.new_workspace(1), zdp.new_state(1.0)
+    zdp.reduce_grad_segment(_replicas_on_device(reps, dt, layout), avg, ws, 0, st)
+    zdp.grad_norm_overflow(None, ws, 1, st)
+    want = oracle.average(reps, ORACLE_DT[dt])
+    assert_bits_equal(down32(avg), want, "average")
+    n2, f = oracle.norm_overflow(want, 1.0)
+    s = zdp.read_state(st)
+    assert s["overflow"] == f == 0 and s["step"] == 0
+    assert abs(s["grad_norm_sq"] - n2) <= NORM_RTOL * n2
+
+
+def test_determinism_run_to_run():
+    outs = []
+    for _ in range(2):
+        n, n_d = 1_000_003, 4
+        master = up32(normal_f32_np(n, 0.02, (12, "m")))
+        m, v = torch.zeros(n, device=DEV), torch.zeros(n, device=DEV)
+        flat = torch.zeros(n, dtype=torch.bfloat16, device=DEV)
+        ws, st = zdp.new_workspace(1), zdp.new_state(1.0)
+        for k in range(2):
+            reps = [up16(grads16_np(n, "bf16", 1.0, (12, k, r)), "bf16") for r in range(n_d)]
+            zdp.adam_step([zdp.Group(master, m, v, replicas=reps, flat_param=flat)], ws, st)
+        torch.cuda.synchronize()
+        outs.append([down32(master), down32(m), down32(v), down16(flat), st.cpu().numpy()])
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a.view(np.uint8), b.view(np.uint8))

@@ -1,0 +1,323 @@
+"""Python binding of libzero_dp.so, the ZeRO-DP partitioned optimizer step for
+AMD MI355X (gfx950).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels. PyTorch supplies device memory (``tensor.data_ptr()``) and the stream
+(``torch.cuda.current_stream()``). Importing this module needs the built
+library; there is no fallback.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libzero_dp.so")
+
+OK = 0
+ERR_INVALID_ARG = -1
+ERR_ALIGNMENT = -2
+ERR_WORKSPACE = -3
+ERR_HIP = -4
+ERR_UNSUPPORTED = -5
+MAX_GROUPS = 8
+MAX_REPLICAS = 4096
+DT_F16 = 1
+DT_BF16 = 2
+
+EXPORTS = ("zero_partition", "zero_partition_tensors", "zero_workspace_bytes",
+           "zero_last_error", "zero_state_init", "zero_reduce_grad_segment",
+           "zero_grad_norm_overflow", "zero_adam_step", "zero_cast_writeback")
+
+
+class ZeroError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"zero_dp error {code}: {msg}")
+        self.code = code
+
+
+class Segment(ctypes.Structure):
+    _fields_ = [("offset", ctypes.c_int64), ("size", ctypes.c_int64)]
+
+
+class TensorSlice(ctypes.Structure):
+    _fields_ = [("tensor", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("shard_begin", ctypes.c_int64), ("tensor_begin", ctypes.c_int64),
+                ("length", ctypes.c_int64)]
+
+
+class StepState(ctypes.Structure):
+    _fields_ = [("beta1_pow", ctypes.c_double * MAX_GROUPS),
+                ("beta2_pow", ctypes.c_double * MAX_GROUPS),
+                ("grad_norm_sq", ctypes.c_double),
+                ("grad_norm", ctypes.c_float),
+                ("loss_scale", ctypes.c_float),
+                ("step", ctypes.c_int64),
+                ("overflow", ctypes.c_int32),
+                ("skipped", ctypes.c_int32),
+                ("good_steps", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class Scaler(ctypes.Structure):
+    _fields_ = [("skip_on_overflow", ctypes.c_int32), ("growth_interval", ctypes.c_int32),
+                ("backoff", ctypes.c_double), ("growth", ctypes.c_double),
+                ("min_scale", ctypes.c_double)]
+
+
+class _Group(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64),
+                ("replicas", ctypes.POINTER(ctypes.c_void_p)),
+                ("n_d", ctypes.c_int32),
+                ("grad_dt", ctypes.c_int32),
+                ("avg", ctypes.c_void_p),
+                ("master", ctypes.c_void_p),
+                ("exp_avg", ctypes.c_void_p),
+                ("exp_avg_sq", ctypes.c_void_p),
+                ("flat_param", ctypes.c_void_p),
+                ("param_offset", ctypes.c_int64),
+                ("param_dt", ctypes.c_int32),
+                ("reserved", ctypes.c_int32),
+                ("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double)]
+
+
+_LIB = None
+
+
+def load():
+    """Load the built library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              f"`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+        L.zero_partition.argtypes = [i64, i32, i64, ctypes.POINTER(Segment), ctypes.POINTER(i64)]
+        L.zero_partition_tensors.argtypes = [ctypes.POINTER(i64), i32, i32, i32, i64,
+                                             ctypes.POINTER(TensorSlice), i32, ctypes.POINTER(i32)]
+        L.zero_workspace_bytes.argtypes = [i32]
+        L.zero_workspace_bytes.restype = ctypes.c_size_t
+        L.zero_last_error.argtypes = []
+        L.zero_last_error.restype = ctypes.c_char_p
+        L.zero_state_init.argtypes = [vp, ctypes.c_float, vp]
+        sz = ctypes.c_size_t
+        L.zero_reduce_grad_segment.argtypes = [ctypes.POINTER(vp), i32, i32, i64, vp, vp, sz, i32, vp, vp]
+        L.zero_grad_norm_overflow.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(i64), i32, i32, vp, sz,
+                                              ctypes.POINTER(Scaler), vp, vp]
+        L.zero_adam_step.argtypes = [ctypes.POINTER(_Group), i32, ctypes.POINTER(Scaler), vp, sz, vp, vp]
+        L.zero_cast_writeback.argtypes = [vp, i64, vp, i64, i32, vp]
+        for name in EXPORTS:
+            fn = getattr(L, name)
+            if name not in ("zero_workspace_bytes", "zero_last_error"):
+                fn.restype = ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def last_error():
+    return load().zero_last_error().decode()
+
+
+def _check(rc):
+    if rc != OK:
+        raise ZeroError(rc, last_error())
+
+
+# --------------------------------------------------------------------------
+# host calls
+# --------------------------------------------------------------------------
+
+def partition(numel, n_d, align_elems=1):
+    """[(offset, size)] for each rank, and the padded length."""
+    segs = (Segment * n_d)()
+    padded = ctypes.c_int64(0)
+    _check(load().zero_partition(numel, n_d, align_elems, segs, ctypes.byref(padded)))
+    return [(s.offset, s.size) for s in segs], padded.value
+
+
+def partition_tensors(numels, n_d, rank, align_elems=1):
+    """[(tensor, shard_begin, tensor_begin, length)] inside rank's segment."""
+    arr = (ctypes.c_int64 * max(1, len(numels)))(*numels)
+    cap = max(1, len(numels))
+    out = (TensorSlice * cap)()
+    n_out = ctypes.c_int32(0)
+    _check(load().zero_partition_tensors(arr, len(numels), n_d, rank, align_elems, out, cap,
+                                         ctypes.byref(n_out)))
+    return [(out[i].tensor, out[i].shard_begin, out[i].tensor_begin, out[i].length)
+            for i in range(n_out.value)]
+
+
+def workspace_bytes(n_groups):
+    return int(load().zero_workspace_bytes(n_groups))
+
+
+# --------------------------------------------------------------------------
+# device calls (torch tensors for memory, torch's current stream)
+# --------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dt(t):
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return DT_F16
+    if t.dtype == torch.bfloat16:
+        return DT_BF16
+    raise TypeError(f"16-bit tensor expected, got {t.dtype}")
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _ptr_array(tensors):
+    return (ctypes.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
+
+
+def new_state(loss_scale=1.0, device="cuda", stream=None):
+    """Allocate and initialise a device zero_step_state (a uint8 tensor)."""
+    torch = _torch()
+    st = torch.empty(ctypes.sizeof(StepState), dtype=torch.uint8, device=device)
+    _check(load().zero_state_init(_ptr(st), float(loss_scale), _stream(stream)))
+    return st
+
+
+def state_init(state, loss_scale=1.0, stream=None):
+    _check(load().zero_state_init(_ptr(state), float(loss_scale), _stream(stream)))
+
+
+def read_state(state):
+    """Copy the device state to the host (synchronises) and decode it."""
+    raw = bytes(state.cpu().numpy().tobytes())
+    s = StepState.from_buffer_copy(raw)
+    return {"beta1_pow": list(s.beta1_pow), "beta2_pow": list(s.beta2_pow),
+            "grad_norm_sq": s.grad_norm_sq, "grad_norm": s.grad_norm, "loss_scale": s.loss_scale,
+            "step": s.step, "overflow": s.overflow, "skipped": s.skipped, "good_steps": s.good_steps}
+
+
+def new_workspace(n_groups, device="cuda"):
+    torch = _torch()
+    nbytes = workspace_bytes(n_groups)
+    if nbytes == 0:
+        raise ValueError(f"n_groups={n_groups} out of range")
+    # torch's caching allocator returns 512-byte aligned blocks
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def scaler(skip_on_overflow=False, growth_interval=1000, backoff=0.5, growth=2.0, min_scale=1.0):
+    return Scaler(int(bool(skip_on_overflow)), int(growth_interval), float(backoff), float(growth),
+                  float(min_scale))
+
+
+def reduce_grad_segment(replicas, avg_out, workspace, group, state, stream=None):
+    """Average N_d gradient copies (list of 16-bit tensors of equal length)."""
+    n = avg_out.numel()
+    for r in replicas:
+        if r.numel() < n:
+            raise ValueError("replica shorter than the shard")
+    arr = _ptr_array(replicas)
+    _check(load().zero_reduce_grad_segment(arr, len(replicas), _dt(replicas[0]), n, _ptr(avg_out),
+                                           _ptr(workspace), _nbytes(workspace), group, _ptr(state),
+                                           _stream(stream)))
+
+
+def grad_norm_overflow(grads, workspace, n_groups, state, scaler_=None, stream=None, grad_dtype=None):
+    """Finalise the norm / overflow flag. ``grads``: None, or a list of n_groups
+    entries (a 16-bit tensor to scan, or None for a slot already filled)."""
+    if grads is None:
+        gp, cp, dt = None, None, DT_F16 if grad_dtype is None else grad_dtype
+    else:
+        if len(grads) != n_groups:
+            raise ValueError("grads must have one entry per group")
+        # an empty gradient still marks its slot for scanning: give it a
+        # non-NULL address (never read, there are no elements)
+        gp = (ctypes.c_void_p * n_groups)(*[
+            (g.data_ptr() or workspace.data_ptr()) if g is not None else 0 for g in grads])
+        cp = (ctypes.c_int64 * n_groups)(*[g.numel() if g is not None else 0 for g in grads])
+        dt = _dt(next(g for g in grads if g is not None))
+    sc = ctypes.byref(scaler_) if scaler_ is not None else None
+    _check(load().zero_grad_norm_overflow(gp, cp, dt, n_groups, _ptr(workspace), _nbytes(workspace), sc,
+                                          _ptr(state), _stream(stream)))
+
+
+@dataclass
+class Group:
+    """One parameter group's shard. Tensors are device tensors."""
+    master: object
+    exp_avg: object
+    exp_avg_sq: object
+    replicas: list = None      # N_d 16-bit tensors (fused average)
+    avg: object = None         # or an fp32 average from reduce_grad_segment
+    flat_param: object = None  # 16-bit flat vector (whole group) or None
+    param_offset: int = 0
+    lr: float = 1e-3
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.0
+
+
+def _group_struct(g, keep):
+    s = _Group()
+    n = g.master.numel()
+    s.n = n
+    if g.replicas is not None:
+        arr = _ptr_array(g.replicas)
+        keep.append(arr)
+        s.replicas = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+        s.n_d = len(g.replicas)
+        s.grad_dt = _dt(g.replicas[0])
+        for r in g.replicas:
+            if r.numel() < n:
+                raise ValueError("replica shorter than the shard")
+    else:
+        s.replicas = None
+        s.n_d = 0
+        s.grad_dt = 0
+    s.avg = g.avg.data_ptr() if g.avg is not None else None
+    for name in ("exp_avg", "exp_avg_sq"):
+        if getattr(g, name).numel() != n:
+            raise ValueError(f"{name} length differs from master")
+    s.master, s.exp_avg, s.exp_avg_sq = g.master.data_ptr(), g.exp_avg.data_ptr(), g.exp_avg_sq.data_ptr()
+    if g.flat_param is not None:
+        if g.param_offset + n > g.flat_param.numel():
+            raise ValueError("param_offset + n exceeds the flat parameter vector")
+        s.flat_param = g.flat_param.data_ptr()
+        s.param_offset = g.param_offset
+        s.param_dt = _dt(g.flat_param)
+    else:
+        s.flat_param = None
+        s.param_offset = 0
+        s.param_dt = 0
+    s.lr, s.beta1, s.beta2, s.eps, s.weight_decay = g.lr, g.beta1, g.beta2, g.eps, g.weight_decay
+    return s
+
+
+def adam_step(groups, workspace, state, scaler_=None, stream=None):
+    keep = []
+    arr = (_Group * len(groups))(*[_group_struct(g, keep) for g in groups])
+    sc = ctypes.byref(scaler_) if scaler_ is not None else None
+    _check(load().zero_adam_step(arr, len(groups), sc, _ptr(workspace), _nbytes(workspace), _ptr(state),
+                                 _stream(stream)))
+
+
+def cast_writeback(master, flat_param, offset, stream=None):
+    n = master.numel()
+    if offset + n > flat_param.numel():
+        raise ValueError("offset + n exceeds the flat parameter vector")
+    _check(load().zero_cast_writeback(_ptr(master), n, _ptr(flat_param), offset, _dt(flat_param),
+                                      _stream(stream)))

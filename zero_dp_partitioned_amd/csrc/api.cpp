@@ -1,0 +1,417 @@
+// Host side of the C ABI (include/zero_dp.h): argument checks, the partition
+// index map, workspace layout, and the order in which kernels are enqueued.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <unordered_map>
+
+#include "zero_dp_internal.h"
+
+using namespace zdp;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(ZERO_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool valid_dt(int32_t dt) { return dt == ZERO_DT_F16 || dt == ZERO_DT_BF16; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Largest of 16/8/4/2 dividing the address.
+int32_t align_class(const void* p) {
+  const uintptr_t u = reinterpret_cast<uintptr_t>(p);
+  if ((u & 15) == 0) return 16;
+  if ((u & 7) == 0) return 8;
+  if ((u & 3) == 0) return 4;
+  return 2;
+}
+
+// The device must be gfx950; checked once per device.
+int check_device() {
+  static std::mutex mu;
+  static std::unordered_map<int, int> ok;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = ok.find(dev);
+  if (it == ok.end()) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    const int is950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    it = ok.emplace(dev, is950).first;
+    if (!is950) snprintf(g_err, sizeof g_err, "device %d is %s, this library is built for gfx950", dev,
+                         prop.gcnArchName);
+  }
+  if (!it->second) return ZERO_ERR_UNSUPPORTED;
+  return ZERO_OK;
+}
+
+Partial* slot_partials(void* ws, int32_t g) {
+  return reinterpret_cast<Partial*>(static_cast<char*>(ws) + kWorkspaceHeader) +
+         static_cast<int64_t>(g) * kMaxBlocks;
+}
+
+int32_t* slot_counts(void* ws) { return static_cast<int32_t*>(ws); }
+
+int check_workspace(size_t have, int32_t slots) {
+  const size_t need = zero_workspace_bytes(slots);
+  if (have < need) return fail(ZERO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", have, need);
+  return ZERO_OK;
+}
+
+bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+// Fill a GradSource from a host array of replica pointers. Sets *vec_ok to
+// whether every replica start is 16-byte aligned (the vector path).
+// An empty shard (n == 0) reads nothing, so its pointers may be NULL.
+int make_source(const void* const* replicas, int32_t n_d, int32_t dt, int64_t n, GradSource* S, bool* vec_ok) {
+  memset(S, 0, sizeof *S);
+  if (!replicas) return fail(ZERO_ERR_INVALID_ARG, "replica pointer array is NULL");
+  if (n_d < 1) return fail(ZERO_ERR_INVALID_ARG, "n_d = %d < 1", n_d);
+  if (n_d > ZERO_MAX_REPLICAS) return fail(ZERO_ERR_UNSUPPORTED, "n_d = %d > %d", n_d, ZERO_MAX_REPLICAS);
+  if (!valid_dt(dt)) return fail(ZERO_ERR_INVALID_ARG, "gradient dtype %d is not f16/bf16", dt);
+  if (n == 0) {
+    S->n_d = n_d;
+    S->nd = static_cast<float>(n_d);
+    *vec_ok = true;
+    return ZERO_OK;
+  }
+  bool va = true;
+  for (int32_t r = 0; r < n_d; ++r) {
+    if (!replicas[r]) return fail(ZERO_ERR_INVALID_ARG, "replica %d is NULL", r);
+    if (!aligned(replicas[r], 2)) return fail(ZERO_ERR_ALIGNMENT, "replica %d is not 2-byte aligned", r);
+    va = va && aligned(replicas[r], 16);
+  }
+  if (n_d <= kInlineReplicas) {
+    for (int32_t r = 0; r < n_d; ++r) S->rep[r] = replicas[r];
+    S->strided = 0;
+  } else {
+    // Beyond the inline table the copies must be equally spaced in one buffer.
+    const char* base = static_cast<const char*>(replicas[0]);
+    const ptrdiff_t d = static_cast<const char*>(replicas[1]) - base;
+    if (d <= 0 || d % 2 != 0)
+      return fail(ZERO_ERR_UNSUPPORTED, "n_d > %d needs equally spaced replicas in one buffer",
+                  kInlineReplicas);
+    for (int32_t r = 2; r < n_d; ++r)
+      if (static_cast<const char*>(replicas[r]) - base != static_cast<ptrdiff_t>(r) * d)
+        return fail(ZERO_ERR_UNSUPPORTED, "n_d > %d needs equally spaced replicas in one buffer",
+                    kInlineReplicas);
+    S->rep[0] = replicas[0];
+    S->stride = d / 2;
+    S->strided = 1;
+  }
+  S->n_d = n_d;
+  S->nd = static_cast<float>(n_d);
+  S->inv_nd = is_pow2(n_d) ? 1.0f / static_cast<float>(n_d) : 0.0f;
+  *vec_ok = va;
+  return ZERO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* zero_last_error(void) { return g_err; }
+
+int zero_partition(int64_t numel, int32_t n_d, int64_t align_elems, zero_segment* segs,
+                   int64_t* padded_numel) {
+  if (numel < 0) return fail(ZERO_ERR_INVALID_ARG, "numel = %lld < 0", (long long)numel);
+  if (n_d < 1) return fail(ZERO_ERR_INVALID_ARG, "n_d = %d < 1", n_d);
+  if (align_elems < 1) return fail(ZERO_ERR_INVALID_ARG, "align_elems < 1");
+  if (!segs) return fail(ZERO_ERR_INVALID_ARG, "segs is NULL");
+  int64_t padded = numel;
+  const int64_t r = numel % align_elems;
+  if (r) {
+    if (numel > INT64_MAX - (align_elems - r)) return fail(ZERO_ERR_INVALID_ARG, "padded numel overflows int64");
+    padded = numel + (align_elems - r);
+  }
+  const int64_t base = padded / n_d, rem = padded % n_d;
+  for (int32_t k = 0; k < n_d; ++k) {
+    segs[k].offset = k * base + (k < rem ? k : rem);
+    segs[k].size = base + (k < rem ? 1 : 0);
+  }
+  if (padded_numel) *padded_numel = padded;
+  return ZERO_OK;
+}
+
+int zero_partition_tensors(const int64_t* numels, int32_t n_tensors, int32_t n_d, int32_t rank,
+                           int64_t align_elems, zero_tensor_slice* out, int32_t cap, int32_t* n_out) {
+  if (!numels && n_tensors > 0) return fail(ZERO_ERR_INVALID_ARG, "numels is NULL");
+  if (n_tensors < 0) return fail(ZERO_ERR_INVALID_ARG, "n_tensors < 0");
+  if (n_d < 1 || rank < 0 || rank >= n_d) return fail(ZERO_ERR_INVALID_ARG, "rank %d out of [0, %d)", rank, n_d);
+  if (!n_out) return fail(ZERO_ERR_INVALID_ARG, "n_out is NULL");
+  int64_t total = 0;
+  for (int32_t t = 0; t < n_tensors; ++t) {
+    if (numels[t] < 0) return fail(ZERO_ERR_INVALID_ARG, "numels[%d] < 0", t);
+    if (total > INT64_MAX - numels[t]) return fail(ZERO_ERR_INVALID_ARG, "total numel overflows int64");
+    total += numels[t];
+  }
+  // the rank's segment, by the same rule as zero_partition
+  int64_t padded = total;
+  if (align_elems < 1) return fail(ZERO_ERR_INVALID_ARG, "align_elems < 1");
+  const int64_t r = total % align_elems;
+  if (r) {
+    if (total > INT64_MAX - (align_elems - r)) return fail(ZERO_ERR_INVALID_ARG, "padded numel overflows int64");
+    padded = total + (align_elems - r);
+  }
+  const int64_t base = padded / n_d, rem = padded % n_d;
+  const int64_t lo = rank * base + (rank < rem ? rank : rem);
+  const int64_t hi = lo + base + (rank < rem ? 1 : 0);
+  int32_t count = 0;
+  int64_t start = 0;
+  for (int32_t t = 0; t < n_tensors; ++t) {
+    const int64_t b = start, e = start + numels[t];
+    start = e;
+    const int64_t ob = b > lo ? b : lo, oe = e < hi ? e : hi;
+    if (ob >= oe) continue;
+    if (count >= cap || !out) return fail(ZERO_ERR_INVALID_ARG, "output capacity %d too small", cap);
+    out[count].tensor = t;
+    out[count].reserved = 0;
+    out[count].shard_begin = ob - lo;
+    out[count].tensor_begin = ob - b;
+    out[count].length = oe - ob;
+    ++count;
+  }
+  *n_out = count;
+  return ZERO_OK;
+}
+
+size_t zero_workspace_bytes(int32_t n_groups) {
+  if (n_groups < 1 || n_groups > ZERO_MAX_GROUPS) return 0;
+  return kWorkspaceHeader + static_cast<size_t>(n_groups) * kMaxBlocks * sizeof(Partial);
+}
+
+int zero_state_init(zero_step_state* state, float loss_scale, void* stream) {
+  if (!state) return fail(ZERO_ERR_INVALID_ARG, "state is NULL");
+  if (!aligned(state, 8)) return fail(ZERO_ERR_ALIGNMENT, "state is not 8-byte aligned");
+  if (!(loss_scale > 0.0f) || loss_scale == __builtin_inff())
+    return fail(ZERO_ERR_INVALID_ARG, "loss_scale must be finite and > 0");
+  if (int rc = check_device()) return rc;
+  hipError_t e = launch_state_init(state, loss_scale, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ZERO_OK : hip_fail(e, "state init launch");
+}
+
+int zero_reduce_grad_segment(const void* const* replicas, int32_t n_d, int32_t grad_dt, int64_t n,
+                             float* avg_out, void* workspace, size_t workspace_bytes, int32_t group,
+                             const zero_step_state* state, void* stream) {
+  if (n < 0) return fail(ZERO_ERR_INVALID_ARG, "n < 0");
+  if (!avg_out && n > 0) return fail(ZERO_ERR_INVALID_ARG, "avg_out is NULL");
+  if (!aligned(avg_out, 4)) return fail(ZERO_ERR_ALIGNMENT, "avg_out is not 4-byte aligned");
+  if (!state) return fail(ZERO_ERR_INVALID_ARG, "state is NULL");
+  if (!workspace) return fail(ZERO_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(ZERO_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (group < 0 || group >= ZERO_MAX_GROUPS) return fail(ZERO_ERR_WORKSPACE, "group %d out of range", group);
+  if (int rc = check_workspace(workspace_bytes, group + 1)) return rc;
+  ReduceArgs R;
+  bool vec = false;
+  if (int rc = make_source(replicas, n_d, grad_dt, n, &R.src, &vec)) return rc;
+  if (int rc = check_device()) return rc;
+  vec = vec && aligned(avg_out, 16);
+  R.n = n;
+  R.avg_out = avg_out;
+  R.state = state;
+  R.partials = slot_partials(workspace, group);
+  R.count = slot_counts(workspace) + group;
+  hipError_t e = launch_reduce(R, grad_dt == ZERO_DT_BF16 ? kSrcBF16 : kSrcF16, vec,
+                               static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ZERO_OK : hip_fail(e, "reduce launch");
+}
+
+int zero_grad_norm_overflow(const void* const* grads, const int64_t* counts, int32_t grad_dt,
+                            int32_t n_groups, void* workspace, size_t workspace_bytes,
+                            const zero_scaler* scaler, zero_step_state* state, void* stream) {
+  if (n_groups < 1 || n_groups > ZERO_MAX_GROUPS)
+    return fail(ZERO_ERR_INVALID_ARG, "n_groups = %d out of [1, %d]", n_groups, ZERO_MAX_GROUPS);
+  if (!state) return fail(ZERO_ERR_INVALID_ARG, "state is NULL");
+  if (!workspace) return fail(ZERO_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(ZERO_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (int rc = check_workspace(workspace_bytes, n_groups)) return rc;
+  ReduceArgs R[ZERO_MAX_GROUPS];
+  bool vec[ZERO_MAX_GROUPS] = {};
+  bool scan[ZERO_MAX_GROUPS] = {};
+  if (grads) {
+    if (!counts) return fail(ZERO_ERR_INVALID_ARG, "counts is NULL");
+    if (!valid_dt(grad_dt)) return fail(ZERO_ERR_INVALID_ARG, "gradient dtype %d is not f16/bf16", grad_dt);
+    for (int32_t g = 0; g < n_groups; ++g) {
+      if (!grads[g]) continue;
+      if (counts[g] < 0) return fail(ZERO_ERR_INVALID_ARG, "counts[%d] < 0", g);
+      const void* one[1] = {grads[g]};
+      if (int rc = make_source(one, 1, grad_dt, counts[g], &R[g].src, &vec[g])) return rc;
+      R[g].n = counts[g];
+      R[g].avg_out = nullptr;
+      R[g].state = state;
+      R[g].partials = slot_partials(workspace, g);
+      R[g].count = slot_counts(workspace) + g;
+      scan[g] = true;
+    }
+  }
+  if (int rc = check_device()) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int src = grad_dt == ZERO_DT_BF16 ? kSrcBF16 : kSrcF16;
+  for (int32_t g = 0; g < n_groups; ++g) {
+    if (!scan[g]) continue;
+    hipError_t e = launch_reduce(R[g], src, vec[g], s);
+    if (e != hipSuccess) return hip_fail(e, "scan launch");
+  }
+  FinalizeArgs F;
+  memset(&F, 0, sizeof F);
+  F.partials = slot_partials(workspace, 0);
+  F.counts = slot_counts(workspace);
+  F.state = state;
+  F.n_groups = n_groups;
+  F.mode = 0;
+  F.skip_on_overflow = scaler ? (scaler->skip_on_overflow != 0) : 0;
+  hipError_t e = launch_finalize(F, s);
+  return e == hipSuccess ? ZERO_OK : hip_fail(e, "finalize launch");
+}
+
+int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_scaler* scaler,
+                   void* workspace, size_t workspace_bytes, zero_step_state* state, void* stream) {
+  if (!groups) return fail(ZERO_ERR_INVALID_ARG, "groups is NULL");
+  if (n_groups < 1 || n_groups > ZERO_MAX_GROUPS)
+    return fail(ZERO_ERR_INVALID_ARG, "n_groups = %d out of [1, %d]", n_groups, ZERO_MAX_GROUPS);
+  if (!state) return fail(ZERO_ERR_INVALID_ARG, "state is NULL");
+  if (!aligned(state, 8)) return fail(ZERO_ERR_ALIGNMENT, "state is not 8-byte aligned");
+  if (!workspace) return fail(ZERO_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(ZERO_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (int rc = check_workspace(workspace_bytes, n_groups)) return rc;
+  const bool dynamic = scaler && scaler->skip_on_overflow;
+  if (dynamic) {
+    if (!(scaler->backoff > 0.0) || !(scaler->growth >= 1.0) || !(scaler->min_scale > 0.0) ||
+        scaler->growth_interval < 0)
+      return fail(ZERO_ERR_INVALID_ARG, "bad loss-scale policy");
+  }
+  AdamArgs A[ZERO_MAX_GROUPS];
+  int src[ZERO_MAX_GROUPS];
+  bool vec[ZERO_MAX_GROUPS];
+  for (int32_t g = 0; g < n_groups; ++g) {
+    const zero_group& G = groups[g];
+    AdamArgs& a = A[g];
+    memset(&a, 0, sizeof a);
+    if (G.n < 0) return fail(ZERO_ERR_INVALID_ARG, "group %d: n < 0", g);
+    if ((!G.master || !G.exp_avg || !G.exp_avg_sq) && G.n > 0)
+      return fail(ZERO_ERR_INVALID_ARG, "group %d: master/exp_avg/exp_avg_sq is NULL", g);
+    if (!aligned(G.master, 4) || !aligned(G.exp_avg, 4) || !aligned(G.exp_avg_sq, 4))
+      return fail(ZERO_ERR_ALIGNMENT, "group %d: fp32 state not 4-byte aligned", g);
+    bool v = aligned(G.master, 16) && aligned(G.exp_avg, 16) && aligned(G.exp_avg_sq, 16);
+    if ((G.replicas != nullptr) == (G.avg != nullptr) && !(G.n == 0 && !G.replicas))
+      return fail(ZERO_ERR_INVALID_ARG, "group %d: give exactly one of replicas and avg", g);
+    if (G.avg || !G.replicas) {
+      if (!aligned(G.avg, 4)) return fail(ZERO_ERR_ALIGNMENT, "group %d: avg not 4-byte aligned", g);
+      a.src.avg = G.avg;
+      a.src.n_d = 1;
+      src[g] = kSrcAvg;
+      v = v && aligned(G.avg, 16);
+    } else {
+      bool rv = false;
+      if (int rc = make_source(G.replicas, G.n_d, G.grad_dt, G.n, &a.src, &rv)) return rc;
+      src[g] = G.grad_dt == ZERO_DT_BF16 ? kSrcBF16 : kSrcF16;
+      v = v && rv;
+    }
+    if (G.flat_param && G.n > 0) {
+      if (!valid_dt(G.param_dt)) return fail(ZERO_ERR_INVALID_ARG, "group %d: param dtype %d", g, G.param_dt);
+      if (G.param_offset < 0) return fail(ZERO_ERR_INVALID_ARG, "group %d: param_offset < 0", g);
+      if (!aligned(G.flat_param, 2)) return fail(ZERO_ERR_ALIGNMENT, "group %d: flat_param not 2-byte aligned", g);
+      a.param = static_cast<uint16_t*>(G.flat_param) + G.param_offset;
+      a.param_dt = G.param_dt;
+      a.param_align = align_class(a.param);
+    }
+    if (!(G.lr >= 0.0) || !(G.beta1 >= 0.0 && G.beta1 < 1.0) || !(G.beta2 >= 0.0 && G.beta2 < 1.0) ||
+        !(G.eps > 0.0) || !(G.weight_decay >= 0.0))
+      return fail(ZERO_ERR_INVALID_ARG, "group %d: hyperparameters out of range", g);
+    a.n = G.n;
+    a.master = G.master;
+    a.m = G.exp_avg;
+    a.v = G.exp_avg_sq;
+    a.beta1_d = G.beta1;
+    a.beta2_d = G.beta2;
+    a.lr = static_cast<float>(G.lr);
+    a.beta1 = static_cast<float>(G.beta1);
+    a.beta2 = static_cast<float>(G.beta2);
+    a.eps = static_cast<float>(G.eps);
+    a.c1 = static_cast<float>(1.0 - G.beta1);
+    a.c2 = static_cast<float>(1.0 - G.beta2);
+    a.decay = static_cast<float>(1.0 - G.lr * G.weight_decay);
+    a.has_decay = G.weight_decay != 0.0;
+    a.group = g;
+    a.state = state;
+    a.partials = slot_partials(workspace, g);
+    a.count = slot_counts(workspace) + g;
+    vec[g] = v;
+  }
+  if (int rc = check_device()) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int32_t g = 0; g < n_groups; ++g) {
+    hipError_t e = launch_adam(A[g], src[g], vec[g], dynamic, s);
+    if (e != hipSuccess) return hip_fail(e, "update launch");
+  }
+  if (!dynamic) {
+    FinalizeArgs F;
+    memset(&F, 0, sizeof F);
+    F.partials = slot_partials(workspace, 0);
+    F.counts = slot_counts(workspace);
+    F.state = state;
+    F.n_groups = n_groups;
+    F.mode = 1;
+    for (int32_t g = 0; g < n_groups; ++g) {
+      F.beta1[g] = groups[g].beta1;
+      F.beta2[g] = groups[g].beta2;
+    }
+    hipError_t e = launch_finalize(F, s);
+    return e == hipSuccess ? ZERO_OK : hip_fail(e, "finalize launch");
+  }
+  CommitArgs C;
+  memset(&C, 0, sizeof C);
+  C.state = state;
+  C.n_groups = n_groups;
+  C.dynamic = 1;
+  C.growth_interval = scaler->growth_interval;
+  C.backoff = scaler->backoff;
+  C.growth = scaler->growth;
+  C.min_scale = scaler->min_scale;
+  for (int32_t g = 0; g < n_groups; ++g) {
+    C.beta1[g] = groups[g].beta1;
+    C.beta2[g] = groups[g].beta2;
+  }
+  hipError_t e = launch_commit(C, s);
+  return e == hipSuccess ? ZERO_OK : hip_fail(e, "commit launch");
+}
+
+int zero_cast_writeback(const float* master, int64_t n, void* flat_param, int64_t offset, int32_t param_dt,
+                        void* stream) {
+  if (n < 0) return fail(ZERO_ERR_INVALID_ARG, "n < 0");
+  if (offset < 0) return fail(ZERO_ERR_INVALID_ARG, "offset < 0");
+  if (!valid_dt(param_dt)) return fail(ZERO_ERR_INVALID_ARG, "param dtype %d is not f16/bf16", param_dt);
+  if (n == 0) return ZERO_OK;  // nothing to write
+  if (!master || !flat_param) return fail(ZERO_ERR_INVALID_ARG, "master or flat_param is NULL");
+  if (!aligned(master, 4)) return fail(ZERO_ERR_ALIGNMENT, "master is not 4-byte aligned");
+  if (!aligned(flat_param, 2)) return fail(ZERO_ERR_ALIGNMENT, "flat_param is not 2-byte aligned");
+  if (int rc = check_device()) return rc;
+  CastArgs C;
+  C.master = master;
+  C.n = n;
+  C.param = static_cast<uint16_t*>(flat_param) + offset;
+  C.param_dt = param_dt;
+  C.param_align = align_class(C.param);
+  hipError_t e = launch_cast(C, aligned(master, 16), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ZERO_OK : hip_fail(e, "cast launch");
+}
+
+}  // extern "C"
