@@ -153,12 +153,12 @@ int zero_partition_tensors(const int64_t* numels, int32_t n_tensors, int32_t n_d
                            int32_t rank, int64_t align_elems, zero_tensor_slice* out,
                            int32_t cap, int32_t* n_out);
 
-/* Bytes of device workspace the step calls need for n_groups groups (norm and
- * overflow partials). Constant in the shard size. 0 if n_groups is out of
- * range. The workspace must be 256-byte aligned; its contents need no
- * initialisation. Every call that takes a workspace also takes its size and
- * returns ZERO_ERR_WORKSPACE if it is smaller than the slots the call uses
- * need (slot g needs zero_workspace_bytes(g + 1)). */
+/* Bytes of device workspace the step calls need for up to n_groups groups:
+ * the gradient-norm partials (about 8 MiB, the same for any shard size and
+ * any n_groups in range). 0 if n_groups is out of range. The workspace must
+ * be 256-byte aligned; its contents need no initialisation. Every call that
+ * takes a workspace also takes its size and returns ZERO_ERR_WORKSPACE if it
+ * is smaller. */
 size_t zero_workspace_bytes(int32_t n_groups);
 
 /* Thread-local text of the last error returned on this thread. */

@@ -32,10 +32,9 @@ bool valid_dt(int32_t dt) { return dt == ZERO_DT_F16 || dt == ZERO_DT_BF16; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// Largest of 16/8/4/2 dividing the address.
+// Largest of 8/4/2 dividing the address (the widest 16-bit store is 8 bytes).
 int32_t align_class(const void* p) {
   const uintptr_t u = reinterpret_cast<uintptr_t>(p);
-  if ((u & 15) == 0) return 16;
   if ((u & 7) == 0) return 8;
   if ((u & 3) == 0) return 4;
   return 2;
@@ -63,16 +62,25 @@ int check_device() {
   return ZERO_OK;
 }
 
-Partial* slot_partials(void* ws, int32_t g) {
-  return reinterpret_cast<Partial*>(static_cast<char*>(ws) + kWorkspaceHeader) +
-         static_cast<int64_t>(g) * kMaxBlocks;
+// Workspace: per-group level-2 partials, then the block partials of the latest launch.
+double* level2_of(void* ws, int32_t g) { return static_cast<double*>(ws) + static_cast<int64_t>(g) * kFoldBlocks; }
+double* scratch_of(void* ws) { return reinterpret_cast<double*>(static_cast<char*>(ws) + kHeaderBytes); }
+
+// Reduce the block partials a streaming launch over n elements just wrote
+// into the level-2 partials of group g.
+hipError_t fold_into(void* ws, int32_t g, int64_t n, hipStream_t s) {
+  FoldArgs F;
+  F.partials = scratch_of(ws);
+  F.count = stream_grid(n);
+  F.level2 = level2_of(ws, g);
+  return launch_fold(F, s);
 }
 
-int32_t* slot_counts(void* ws) { return static_cast<int32_t*>(ws); }
-
-int check_workspace(size_t have, int32_t slots) {
-  const size_t need = zero_workspace_bytes(slots);
-  if (have < need) return fail(ZERO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", have, need);
+int check_workspace(const void* ws, size_t have) {
+  if (!ws) return fail(ZERO_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(ZERO_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (have < kWorkspaceBytes)
+    return fail(ZERO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", have, kWorkspaceBytes);
   return ZERO_OK;
 }
 
@@ -97,7 +105,7 @@ int make_source(const void* const* replicas, int32_t n_d, int32_t dt, int64_t n,
   for (int32_t r = 0; r < n_d; ++r) {
     if (!replicas[r]) return fail(ZERO_ERR_INVALID_ARG, "replica %d is NULL", r);
     if (!aligned(replicas[r], 2)) return fail(ZERO_ERR_ALIGNMENT, "replica %d is not 2-byte aligned", r);
-    va = va && aligned(replicas[r], 16);
+    va = va && aligned(replicas[r], 8);
   }
   if (n_d <= kInlineReplicas) {
     for (int32_t r = 0; r < n_d; ++r) S->rep[r] = replicas[r];
@@ -195,7 +203,7 @@ int zero_partition_tensors(const int64_t* numels, int32_t n_tensors, int32_t n_d
 
 size_t zero_workspace_bytes(int32_t n_groups) {
   if (n_groups < 1 || n_groups > ZERO_MAX_GROUPS) return 0;
-  return kWorkspaceHeader + static_cast<size_t>(n_groups) * kMaxBlocks * sizeof(Partial);
+  return kWorkspaceBytes;
 }
 
 int zero_state_init(zero_step_state* state, float loss_scale, void* stream) {
@@ -215,10 +223,8 @@ int zero_reduce_grad_segment(const void* const* replicas, int32_t n_d, int32_t g
   if (!avg_out && n > 0) return fail(ZERO_ERR_INVALID_ARG, "avg_out is NULL");
   if (!aligned(avg_out, 4)) return fail(ZERO_ERR_ALIGNMENT, "avg_out is not 4-byte aligned");
   if (!state) return fail(ZERO_ERR_INVALID_ARG, "state is NULL");
-  if (!workspace) return fail(ZERO_ERR_WORKSPACE, "workspace is NULL");
-  if (!aligned(workspace, 256)) return fail(ZERO_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (int rc = check_workspace(workspace, workspace_bytes)) return rc;
   if (group < 0 || group >= ZERO_MAX_GROUPS) return fail(ZERO_ERR_WORKSPACE, "group %d out of range", group);
-  if (int rc = check_workspace(workspace_bytes, group + 1)) return rc;
   ReduceArgs R;
   bool vec = false;
   if (int rc = make_source(replicas, n_d, grad_dt, n, &R.src, &vec)) return rc;
@@ -227,11 +233,12 @@ int zero_reduce_grad_segment(const void* const* replicas, int32_t n_d, int32_t g
   R.n = n;
   R.avg_out = avg_out;
   R.state = state;
-  R.partials = slot_partials(workspace, group);
-  R.count = slot_counts(workspace) + group;
-  hipError_t e = launch_reduce(R, grad_dt == ZERO_DT_BF16 ? kSrcBF16 : kSrcF16, vec,
-                               static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? ZERO_OK : hip_fail(e, "reduce launch");
+  R.partials = scratch_of(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_reduce(R, grad_dt == ZERO_DT_BF16 ? kSrcBF16 : kSrcF16, vec, s);
+  if (e != hipSuccess) return hip_fail(e, "reduce launch");
+  e = fold_into(workspace, group, n, s);
+  return e == hipSuccess ? ZERO_OK : hip_fail(e, "fold launch");
 }
 
 int zero_grad_norm_overflow(const void* const* grads, const int64_t* counts, int32_t grad_dt,
@@ -240,9 +247,7 @@ int zero_grad_norm_overflow(const void* const* grads, const int64_t* counts, int
   if (n_groups < 1 || n_groups > ZERO_MAX_GROUPS)
     return fail(ZERO_ERR_INVALID_ARG, "n_groups = %d out of [1, %d]", n_groups, ZERO_MAX_GROUPS);
   if (!state) return fail(ZERO_ERR_INVALID_ARG, "state is NULL");
-  if (!workspace) return fail(ZERO_ERR_WORKSPACE, "workspace is NULL");
-  if (!aligned(workspace, 256)) return fail(ZERO_ERR_WORKSPACE, "workspace is not 256-byte aligned");
-  if (int rc = check_workspace(workspace_bytes, n_groups)) return rc;
+  if (int rc = check_workspace(workspace, workspace_bytes)) return rc;
   ReduceArgs R[ZERO_MAX_GROUPS];
   bool vec[ZERO_MAX_GROUPS] = {};
   bool scan[ZERO_MAX_GROUPS] = {};
@@ -257,8 +262,7 @@ int zero_grad_norm_overflow(const void* const* grads, const int64_t* counts, int
       R[g].n = counts[g];
       R[g].avg_out = nullptr;
       R[g].state = state;
-      R[g].partials = slot_partials(workspace, g);
-      R[g].count = slot_counts(workspace) + g;
+      R[g].partials = scratch_of(workspace);
       scan[g] = true;
     }
   }
@@ -269,11 +273,12 @@ int zero_grad_norm_overflow(const void* const* grads, const int64_t* counts, int
     if (!scan[g]) continue;
     hipError_t e = launch_reduce(R[g], src, vec[g], s);
     if (e != hipSuccess) return hip_fail(e, "scan launch");
+    e = fold_into(workspace, g, R[g].n, s);
+    if (e != hipSuccess) return hip_fail(e, "fold launch");
   }
   FinalizeArgs F;
   memset(&F, 0, sizeof F);
-  F.partials = slot_partials(workspace, 0);
-  F.counts = slot_counts(workspace);
+  F.level2 = level2_of(workspace, 0);
   F.state = state;
   F.n_groups = n_groups;
   F.mode = 0;
@@ -289,9 +294,7 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_scaler
     return fail(ZERO_ERR_INVALID_ARG, "n_groups = %d out of [1, %d]", n_groups, ZERO_MAX_GROUPS);
   if (!state) return fail(ZERO_ERR_INVALID_ARG, "state is NULL");
   if (!aligned(state, 8)) return fail(ZERO_ERR_ALIGNMENT, "state is not 8-byte aligned");
-  if (!workspace) return fail(ZERO_ERR_WORKSPACE, "workspace is NULL");
-  if (!aligned(workspace, 256)) return fail(ZERO_ERR_WORKSPACE, "workspace is not 256-byte aligned");
-  if (int rc = check_workspace(workspace_bytes, n_groups)) return rc;
+  if (int rc = check_workspace(workspace, workspace_bytes)) return rc;
   const bool dynamic = scaler && scaler->skip_on_overflow;
   if (dynamic) {
     if (!(scaler->backoff > 0.0) || !(scaler->growth >= 1.0) || !(scaler->min_scale > 0.0) ||
@@ -352,8 +355,7 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_scaler
     a.has_decay = G.weight_decay != 0.0;
     a.group = g;
     a.state = state;
-    a.partials = slot_partials(workspace, g);
-    a.count = slot_counts(workspace) + g;
+    a.partials = dynamic ? nullptr : scratch_of(workspace);
     vec[g] = v;
   }
   if (int rc = check_device()) return rc;
@@ -361,12 +363,15 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_scaler
   for (int32_t g = 0; g < n_groups; ++g) {
     hipError_t e = launch_adam(A[g], src[g], vec[g], dynamic, s);
     if (e != hipSuccess) return hip_fail(e, "update launch");
+    if (!dynamic) {
+      e = fold_into(workspace, g, A[g].n, s);
+      if (e != hipSuccess) return hip_fail(e, "fold launch");
+    }
   }
   if (!dynamic) {
     FinalizeArgs F;
     memset(&F, 0, sizeof F);
-    F.partials = slot_partials(workspace, 0);
-    F.counts = slot_counts(workspace);
+    F.level2 = level2_of(workspace, 0);
     F.state = state;
     F.n_groups = n_groups;
     F.mode = 1;

@@ -1,20 +1,27 @@
 // gfx950 (CDNA4) kernels of the ZeRO-DP partitioned optimizer step.
 //
-// The step is a bandwidth-bound elementwise pass plus two small reductions, so
-// these are streaming kernels: 64-lane wavefronts, 256-thread blocks, a
-// grid-stride loop over 8 elements per thread per iteration (one 16-byte load
-// per 16-bit gradient copy, two 16-byte loads per fp32 state array), a grid
-// sized to what stays resident on the 256 CUs, and no matrix cores.
+// The step is a bandwidth-bound elementwise pass plus a norm reduction, so
+// these are streaming kernels without matrix cores. Layout (see
+// zero_dp_internal.h): 256-thread blocks own 4096-element tiles and walk them
+// as 4-element quads, lane l on quads l, l+256, l+512, l+768, so every
+// wavefront load or store is one contiguous 1 KiB (fp32) or 512 B (16-bit)
+// run. One block per tile: the hardware dispatcher hands out tiles in order,
+// which keeps the resident blocks on one advancing window of HBM; on gfx950
+// this sustains clearly more bandwidth for a read-modify-write stream than a
+// resident grid looping over the vector.
 //
 // Numerics follow the per-coordinate Adam update of the ZeRO reading notes
 // (second part, §3) in fp32 with one rounding per operation: fp-contract is off
 // for this file, division and square root are the correctly rounded IEEE
 // operations, and the fp32 -> 16-bit writeback rounds to nearest even.
+//
+// Norm and overflow flag: every block writes one fp64 partial (sum of g^2 of
+// its elements, or NaN if one of its averaged gradients was inf/NaN); a fold
+// kernel reduces a launch's partials into 256 per-group values, and a one-block
+// kernel combines those. Every reduction has a fixed shape, so the norm is the
+// same bit pattern run after run.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-
-#include <mutex>
-#include <unordered_map>
 
 #include "zero_dp_internal.h"
 
@@ -23,25 +30,21 @@
 namespace zdp {
 namespace {
 
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned u2 __attribute__((ext_vector_type(2)));
+
 // ------------------------------------------------------------------------
 // 16-bit encodings
 // ------------------------------------------------------------------------
 
-__device__ __forceinline__ float f16_to_f32(uint32_t h) {
-  _Float16 x = __builtin_bit_cast(_Float16, static_cast<uint16_t>(h));
-  return static_cast<float>(x);
-}
-
-__device__ __forceinline__ float bf16_to_f32(uint32_t h) {
-  return __uint_as_float(h << 16);
-}
-
 template <int DT>
 __device__ __forceinline__ float decode16(uint32_t h) {
-  if constexpr (DT == kSrcBF16)
-    return bf16_to_f32(h);
-  else
-    return f16_to_f32(h);
+  if constexpr (DT == kSrcBF16) {
+    return __uint_as_float(h << 16);
+  } else {
+    const _Float16 x = __builtin_bit_cast(_Float16, static_cast<uint16_t>(h));
+    return static_cast<float>(x);
+  }
 }
 
 // fp32 -> 16 bits, round to nearest even, NaN -> canonical quiet NaN.
@@ -52,30 +55,24 @@ __device__ __forceinline__ uint32_t encode16(float x, int dt) {
     u += 0x7FFFu + ((u >> 16) & 1u);
     return u >> 16;
   }
-  _Float16 h = static_cast<_Float16>(x);
+  const _Float16 h = static_cast<_Float16>(x);
   return __builtin_bit_cast(uint16_t, h);
 }
 
-// Write 8 consecutive 16-bit values at element pointer p (byte alignment `al`).
-__device__ __forceinline__ void store8_16(void* p, const uint32_t h[8], int al) {
+// Four consecutive 16-bit values at p, with p's byte alignment `al` (8, 4, 2).
+__device__ __forceinline__ void store4_16(uint16_t* p, const uint32_t h[4], int al) {
   const uint32_t w0 = h[0] | (h[1] << 16), w1 = h[2] | (h[3] << 16);
-  const uint32_t w2 = h[4] | (h[5] << 16), w3 = h[6] | (h[7] << 16);
-  if (al >= 16) {
-    *reinterpret_cast<uint4*>(p) = make_uint4(w0, w1, w2, w3);
-  } else if (al == 8) {
-    uint2* q = reinterpret_cast<uint2*>(p);
-    q[0] = make_uint2(w0, w1);
-    q[1] = make_uint2(w2, w3);
+  if (al >= 8) {
+    u2 w;
+    w.x = w0;
+    w.y = w1;
+    *reinterpret_cast<u2*>(p) = w;
   } else if (al == 4) {
-    uint32_t* q = reinterpret_cast<uint32_t*>(p);
-    q[0] = w0;
-    q[1] = w1;
-    q[2] = w2;
-    q[3] = w3;
+    reinterpret_cast<uint32_t*>(p)[0] = w0;
+    reinterpret_cast<uint32_t*>(p)[1] = w1;
   } else {
-    uint16_t* q = reinterpret_cast<uint16_t*>(p);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) q[k] = static_cast<uint16_t>(h[k]);
+    for (int k = 0; k < 4; ++k) p[k] = static_cast<uint16_t>(h[k]);
   }
 }
 
@@ -84,21 +81,17 @@ __device__ __forceinline__ void store8_16(void* p, const uint32_t h[8], int al) 
 //   acc = 0; acc += float(copy_r[j]) for r in order; a = acc / N_d
 // ------------------------------------------------------------------------
 
-template <int DT>
 __device__ __forceinline__ const uint16_t* replica(const GradSource& S, int r) {
-  if (S.strided)
-    return static_cast<const uint16_t*>(S.rep[0]) + static_cast<int64_t>(r) * S.stride;
+  if (S.strided) return static_cast<const uint16_t*>(S.rep[0]) + static_cast<int64_t>(r) * S.stride;
   return static_cast<const uint16_t*>(S.rep[r]);
 }
 
 template <int DT>
-__device__ __forceinline__ void accumulate8(float acc[8], uint4 x) {
-  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    acc[2 * k] = acc[2 * k] + decode16<DT>(w[k] & 0xFFFFu);
-    acc[2 * k + 1] = acc[2 * k + 1] + decode16<DT>(w[k] >> 16);
-  }
+__device__ __forceinline__ void accumulate4(float acc[4], u2 x) {
+  acc[0] = acc[0] + decode16<DT>(x.x & 0xFFFFu);
+  acc[1] = acc[1] + decode16<DT>(x.x >> 16);
+  acc[2] = acc[2] + decode16<DT>(x.y & 0xFFFFu);
+  acc[3] = acc[3] + decode16<DT>(x.y >> 16);
 }
 
 __device__ __forceinline__ float finish_average(float acc, const GradSource& S) {
@@ -107,37 +100,30 @@ __device__ __forceinline__ float finish_average(float acc, const GradSource& S) 
   return acc / S.nd;
 }
 
-// Averaged gradient of elements j .. j+7 (16-byte aligned vector path).
+// Averaged gradient of elements e .. e+3 (aligned quad path).
 template <int SRC>
-__device__ __forceinline__ void source8(const GradSource& S, int64_t j, float a[8]) {
+__device__ __forceinline__ void source4(const GradSource& S, int64_t e, float a[4]) {
   if constexpr (SRC == kSrcAvg) {
-    const float4 x0 = *reinterpret_cast<const float4*>(S.avg + j);
-    const float4 x1 = *reinterpret_cast<const float4*>(S.avg + j + 4);
-    a[0] = x0.x; a[1] = x0.y; a[2] = x0.z; a[3] = x0.w;
-    a[4] = x1.x; a[5] = x1.y; a[6] = x1.z; a[7] = x1.w;
+    const f4 x = *reinterpret_cast<const f4*>(S.avg + e);
+    a[0] = x.x;
+    a[1] = x.y;
+    a[2] = x.z;
+    a[3] = x.w;
   } else {
-    float acc[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     const int nd = S.n_d;
     int r = 0;
-    // Four copies in flight per step; the additions stay in replica order.
-    for (; r + 4 <= nd; r += 4) {
-      const uint4 x0 = *reinterpret_cast<const uint4*>(replica<SRC>(S, r) + j);
-      const uint4 x1 = *reinterpret_cast<const uint4*>(replica<SRC>(S, r + 1) + j);
-      const uint4 x2 = *reinterpret_cast<const uint4*>(replica<SRC>(S, r + 2) + j);
-      const uint4 x3 = *reinterpret_cast<const uint4*>(replica<SRC>(S, r + 3) + j);
-      accumulate8<SRC>(acc, x0);
-      accumulate8<SRC>(acc, x1);
-      accumulate8<SRC>(acc, x2);
-      accumulate8<SRC>(acc, x3);
-    }
-    for (; r < nd; ++r) {
-      const uint4 x = *reinterpret_cast<const uint4*>(replica<SRC>(S, r) + j);
-      accumulate8<SRC>(acc, x);
-    }
+    // eight copies in flight at a time; the additions stay in replica order
+    for (; r + 8 <= nd; r += 8) {
+      u2 x[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) a[k] = finish_average(acc[k], S);
+      for (int q = 0; q < 8; ++q) x[q] = *reinterpret_cast<const u2*>(replica(S, r + q) + e);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) accumulate4<SRC>(acc, x[q]);
+    }
+    for (; r < nd; ++r) accumulate4<SRC>(acc, *reinterpret_cast<const u2*>(replica(S, r) + e));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] = finish_average(acc[k], S);
   }
 }
 
@@ -148,7 +134,7 @@ __device__ __forceinline__ float source1(const GradSource& S, int64_t j) {
     return S.avg[j];
   } else {
     float acc = 0.0f;
-    for (int r = 0; r < S.n_d; ++r) acc = acc + decode16<SRC>(replica<SRC>(S, r)[j]);
+    for (int r = 0; r < S.n_d; ++r) acc = acc + decode16<SRC>(replica(S, r)[j]);
     return finish_average(acc, S);
   }
 }
@@ -166,7 +152,7 @@ __device__ __forceinline__ Scalars load_scalars(const AdamArgs& A) {
   const zero_step_state* st = A.state;
   Scalars s;
   s.inv_scale = static_cast<float>(1.0 / static_cast<double>(st->loss_scale));
-  // beta^t for the step being applied: the stored beta^(t-1) times beta, in fp64
+  // beta^t of the step being applied: the stored beta^(t-1) times beta, in fp64
   s.b1 = static_cast<float>(1.0 - st->beta1_pow[A.group] * A.beta1_d);
   s.b2 = static_cast<float>(1.0 - st->beta2_pow[A.group] * A.beta2_d);
   s.beta1 = A.beta1;
@@ -194,19 +180,22 @@ __device__ __forceinline__ void adam1(float g, float& th, float& m, float& v, co
   v = vt;
 }
 
-// ------------------------------------------------------------------------
-// Block reduction of the norm / overflow partials (wavefront butterfly, then
-// the four wavefronts of the block through LDS), written to the group's slot.
-// ------------------------------------------------------------------------
+// Norm / overflow contribution of one averaged gradient.
+__device__ __forceinline__ void account(float a, float g, double& sumsq, int& bad) {
+  bad |= !__builtin_isfinite(a);
+  const double gd = static_cast<double>(g);
+  sumsq = __builtin_fma(gd, gd, sumsq);
+}
 
-__device__ __forceinline__ void write_partial(double s, int bad, Partial* out, int32_t* count) {
+// One fp64 partial per block: wavefront butterfly, then the block's four
+// wavefronts through LDS in a fixed order. NaN marks a non-finite gradient.
+__device__ __forceinline__ void write_block_partial(double s, int bad, double* out) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
   const int any_bad = __any(bad);
   __shared__ double ws[kBlock / 64];
   __shared__ int wf[kBlock / 64];
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (lane == 0) {
     ws[w] = s;
     wf[w] = any_bad;
@@ -220,19 +209,15 @@ __device__ __forceinline__ void write_partial(double s, int bad, Partial* out, i
       t += ws[k];
       f |= wf[k];
     }
-    Partial p;
-    p.sumsq = t;
-    p.flag = f ? 1 : 0;
-    p.pad = 0;
-    out[blockIdx.x] = p;
-    if (blockIdx.x == 0) *count = static_cast<int32_t>(gridDim.x);
+    out[blockIdx.x] = f ? __builtin_nan("") : t;
   }
 }
 
 // ------------------------------------------------------------------------
-// The fused / checked update kernel
-//   CHECKED = false: average, overflow + norm partials, Adam, writeback.
-//   CHECKED = true : exits if the step was voided; no partials.
+// The update kernel
+//   CHECKED = false (fused): average, norm partials, Adam, writeback.
+//   CHECKED = true: exits if the step was voided; no partials.
+// VEC: fp32 arrays 16-byte and 16-bit copies 8-byte aligned (quad path).
 // ------------------------------------------------------------------------
 
 template <int SRC, bool VEC, bool CHECKED>
@@ -243,77 +228,63 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs A) {
   const Scalars s = load_scalars(A);
   double sumsq = 0.0;
   int bad = 0;
-  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-  const int64_t nthreads = static_cast<int64_t>(gridDim.x) * kBlock;
   const int pdt = A.param_dt;
-  char* const param = static_cast<char*>(A.param);
+  uint16_t* const param = static_cast<uint16_t*>(A.param);
+  const int64_t n = A.n;
+  const int64_t ntiles = (n + kTile - 1) / kTile;
 
   auto one = [&](int64_t j) {
     const float a = source1<SRC>(A.src, j);
     const float g = a * s.inv_scale;
-    if constexpr (!CHECKED) {
-      bad |= !__builtin_isfinite(a);
-      const double gd = static_cast<double>(g);
-      sumsq = __builtin_fma(gd, gd, sumsq);
-    }
+    if constexpr (!CHECKED) account(a, g, sumsq, bad);
     float th = A.master[j], m = A.m[j], v = A.v[j];
     adam1(g, th, m, v, s);
     A.master[j] = th;
     A.m[j] = m;
     A.v[j] = v;
-    if (pdt) reinterpret_cast<uint16_t*>(param)[j] = static_cast<uint16_t>(encode16(th, pdt));
+    if (pdt) param[j] = static_cast<uint16_t>(encode16(th, pdt));
   };
 
-  if constexpr (VEC) {
-    const int64_t nv = A.n / kVec;
-    for (int64_t i = tid; i < nv; i += nthreads) {
-      const int64_t j = i * kVec;
-      float a[8];
-      source8<SRC>(A.src, j, a);
-      const float4 t0 = *reinterpret_cast<const float4*>(A.master + j);
-      const float4 t1 = *reinterpret_cast<const float4*>(A.master + j + 4);
-      const float4 m0 = *reinterpret_cast<const float4*>(A.m + j);
-      const float4 m1 = *reinterpret_cast<const float4*>(A.m + j + 4);
-      const float4 v0 = *reinterpret_cast<const float4*>(A.v + j);
-      const float4 v1 = *reinterpret_cast<const float4*>(A.v + j + 4);
-      float th[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
-      float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-      float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float g = a[k] * s.inv_scale;
-        if constexpr (!CHECKED) {
-          bad |= !__builtin_isfinite(a[k]);
-          const double gd = static_cast<double>(g);
-          sumsq = __builtin_fma(gd, gd, sumsq);
+    for (int k = 0; k < kQuadsPerThread; ++k) {
+      const int64_t e = t * kTile + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4;
+      if (VEC && e + 4 <= n) {
+        float a[4];
+        source4<SRC>(A.src, e, a);
+        const f4 t4 = *reinterpret_cast<const f4*>(A.master + e);
+        const f4 m4 = *reinterpret_cast<const f4*>(A.m + e);
+        const f4 v4 = *reinterpret_cast<const f4*>(A.v + e);
+        float th[4] = {t4.x, t4.y, t4.z, t4.w};
+        float mm[4] = {m4.x, m4.y, m4.z, m4.w};
+        float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float g = a[q] * s.inv_scale;
+          if constexpr (!CHECKED) account(a[q], g, sumsq, bad);
+          adam1(g, th[q], mm[q], vv[q], s);
         }
-        adam1(g, th[k], mm[k], vv[k], s);
-      }
-      *reinterpret_cast<float4*>(A.master + j) = make_float4(th[0], th[1], th[2], th[3]);
-      *reinterpret_cast<float4*>(A.master + j + 4) = make_float4(th[4], th[5], th[6], th[7]);
-      *reinterpret_cast<float4*>(A.m + j) = make_float4(mm[0], mm[1], mm[2], mm[3]);
-      *reinterpret_cast<float4*>(A.m + j + 4) = make_float4(mm[4], mm[5], mm[6], mm[7]);
-      *reinterpret_cast<float4*>(A.v + j) = make_float4(vv[0], vv[1], vv[2], vv[3]);
-      *reinterpret_cast<float4*>(A.v + j + 4) = make_float4(vv[4], vv[5], vv[6], vv[7]);
-      if (pdt) {
-        uint32_t h[8];
+        *reinterpret_cast<f4*>(A.master + e) = (f4){th[0], th[1], th[2], th[3]};
+        *reinterpret_cast<f4*>(A.m + e) = (f4){mm[0], mm[1], mm[2], mm[3]};
+        *reinterpret_cast<f4*>(A.v + e) = (f4){vv[0], vv[1], vv[2], vv[3]};
+        if (pdt) {
+          uint32_t h[4];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) h[k] = encode16(th[k], pdt);
-        store8_16(param + 2 * j, h, A.param_align);
+          for (int q = 0; q < 4; ++q) h[q] = encode16(th[q], pdt);
+          store4_16(param + e, h, A.param_align);
+        }
+      } else {
+        for (int q = 0; q < 4; ++q)
+          if (e + q < n) one(e + q);
       }
     }
-    // ragged tail: fewer than 8 elements, one per thread
-    const int64_t j = nv * kVec + tid;
-    if (j < A.n) one(j);
-  } else {
-    for (int64_t j = tid; j < A.n; j += nthreads) one(j);
   }
-  if constexpr (!CHECKED) write_partial(sumsq, bad, A.partials, A.count);
+  if constexpr (!CHECKED) write_block_partial(sumsq, bad, A.partials);
 }
 
 // ------------------------------------------------------------------------
-// Average-only pass (checked pipeline) and single-copy scan: writes the fp32
-// average (if avg_out) and the norm / overflow partials.
+// Average-only pass (checked pipeline) and single-copy scan: the fp32 average
+// (if avg_out) and the norm / overflow partials.
 // ------------------------------------------------------------------------
 
 template <int SRC, bool VEC>
@@ -321,81 +292,74 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(const ReduceArgs R) {
   const float inv_scale = static_cast<float>(1.0 / static_cast<double>(R.state->loss_scale));
   double sumsq = 0.0;
   int bad = 0;
-  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-  const int64_t nthreads = static_cast<int64_t>(gridDim.x) * kBlock;
   float* const out = R.avg_out;
-  auto one = [&](int64_t j) {
-    const float a = source1<SRC>(R.src, j);
-    bad |= !__builtin_isfinite(a);
-    const double gd = static_cast<double>(a * inv_scale);
-    sumsq = __builtin_fma(gd, gd, sumsq);
-    if (out) out[j] = a;
-  };
-  if constexpr (VEC) {
-    const int64_t nv = R.n / kVec;
-    for (int64_t i = tid; i < nv; i += nthreads) {
-      const int64_t j = i * kVec;
-      float a[8];
-      source8<SRC>(R.src, j, a);
+  const int64_t n = R.n;
+  const int64_t ntiles = (n + kTile - 1) / kTile;
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        bad |= !__builtin_isfinite(a[k]);
-        const double gd = static_cast<double>(a[k] * inv_scale);
-        sumsq = __builtin_fma(gd, gd, sumsq);
-      }
-      if (out) {
-        *reinterpret_cast<float4*>(out + j) = make_float4(a[0], a[1], a[2], a[3]);
-        *reinterpret_cast<float4*>(out + j + 4) = make_float4(a[4], a[5], a[6], a[7]);
+    for (int k = 0; k < kQuadsPerThread; ++k) {
+      const int64_t e = t * kTile + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4;
+      if (VEC && e + 4 <= n) {
+        float a[4];
+        source4<SRC>(R.src, e, a);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) account(a[q], a[q] * inv_scale, sumsq, bad);
+        if (out) *reinterpret_cast<f4*>(out + e) = (f4){a[0], a[1], a[2], a[3]};
+      } else {
+        for (int q = 0; q < 4; ++q) {
+          if (e + q >= n) break;
+          const float a = source1<SRC>(R.src, e + q);
+          account(a, a * inv_scale, sumsq, bad);
+          if (out) out[e + q] = a;
+        }
       }
     }
-    const int64_t j = nv * kVec + tid;
-    if (j < R.n) one(j);
-  } else {
-    for (int64_t j = tid; j < R.n; j += nthreads) one(j);
   }
-  write_partial(sumsq, bad, R.partials, R.count);
+  write_block_partial(sumsq, bad, R.partials);
 }
 
 // ------------------------------------------------------------------------
-// One-block kernels: combine partials, state bookkeeping
+// Fold: block j of kFoldBlocks sums partials [j*C, min((j+1)*C, count)) with
+// C = ceil(count / kFoldBlocks), thread i taking i, i+256, ... of the range.
 // ------------------------------------------------------------------------
 
-constexpr int kFinalizeThreads = 1024;
-
-__global__ void __launch_bounds__(kFinalizeThreads) finalize_kernel(const FinalizeArgs F) {
-  double s = 0.0;
-  int f = 0;
-  for (int g = 0; g < F.n_groups; ++g) {
-    const Partial* p = F.partials + static_cast<int64_t>(g) * kMaxBlocks;
-    int cnt = F.counts[g];  // written by the pass that filled the slot
-    cnt = cnt < 0 ? 0 : (cnt > kMaxBlocks ? kMaxBlocks : cnt);
-    for (int i = threadIdx.x; i < cnt; i += kFinalizeThreads) {
-      s += p[i].sumsq;
-      f |= p[i].flag;
-    }
-  }
+__device__ __forceinline__ double block_sum(double s) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-  const int any_bad = __any(f);
-  __shared__ double ws[kFinalizeThreads / 64];
-  __shared__ int wf[kFinalizeThreads / 64];
+  __shared__ double ws[kBlock / 64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  if (lane == 0) {
-    ws[w] = s;
-    wf[w] = any_bad;
-  }
+  if (lane == 0) ws[w] = s;
   __syncthreads();
-  if (threadIdx.x != 0) return;
   double t = 0.0;
-  int flag = 0;
-  for (int k = 0; k < kFinalizeThreads / 64; ++k) {
-    t += ws[k];
-    flag |= wf[k];
-  }
+#pragma unroll
+  for (int k = 0; k < kBlock / 64; ++k) t += ws[k];
+  __syncthreads();
+  return t;
+}
+
+__global__ void __launch_bounds__(kBlock) fold_kernel(const FoldArgs F) {
+  const int64_t per = (F.count + kFoldBlocks - 1) / kFoldBlocks;
+  const int64_t lo = static_cast<int64_t>(blockIdx.x) * per;
+  const int64_t hi = lo + per < F.count ? lo + per : F.count;
+  double s = 0.0;
+  for (int64_t i = lo + threadIdx.x; i < hi; i += kBlock) s += F.partials[i];
+  const double t = block_sum(s);
+  if (threadIdx.x == 0) F.level2[blockIdx.x] = t;
+}
+
+// ------------------------------------------------------------------------
+// One-block kernels: combine the groups' level-2 partials, state bookkeeping
+// ------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(kBlock) finalize_kernel(const FinalizeArgs F) {
+  double total = 0.0;
+  for (int g = 0; g < F.n_groups; ++g) total += block_sum(F.level2[g * kFoldBlocks + threadIdx.x]);
+  if (threadIdx.x != 0) return;
   zero_step_state* st = F.state;
-  st->grad_norm_sq = t;
-  st->grad_norm = static_cast<float>(__builtin_sqrt(t));
-  st->overflow = flag ? 1 : 0;
+  const int flag = __builtin_isnan(total) ? 1 : 0;  // a non-finite gradient poisons its partial
+  st->grad_norm_sq = total;
+  st->grad_norm = static_cast<float>(__builtin_sqrt(total));
+  st->overflow = flag;
   if (F.mode == 1) {
     // static loss scale: the update was applied whatever the flag says
     st->skipped = 0;
@@ -455,81 +419,35 @@ __global__ void state_init_kernel(zero_step_state* st, float loss_scale) {
 
 template <bool VEC>
 __global__ void __launch_bounds__(kBlock) cast_kernel(const CastArgs C) {
-  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-  const int64_t nthreads = static_cast<int64_t>(gridDim.x) * kBlock;
-  char* const param = static_cast<char*>(C.param);
   uint16_t* const p16 = static_cast<uint16_t*>(C.param);
-  if constexpr (VEC) {
-    const int64_t nv = C.n / kVec;
-    for (int64_t i = tid; i < nv; i += nthreads) {
-      const int64_t j = i * kVec;
-      const float4 x0 = *reinterpret_cast<const float4*>(C.master + j);
-      const float4 x1 = *reinterpret_cast<const float4*>(C.master + j + 4);
-      const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-      uint32_t h[8];
+  const int64_t n = C.n;
+  const int64_t ntiles = (n + kTile - 1) / kTile;
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) h[k] = encode16(x[k], C.param_dt);
-      store8_16(param + 2 * j, h, C.param_align);
+    for (int k = 0; k < kQuadsPerThread; ++k) {
+      const int64_t e = t * kTile + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4;
+      if (VEC && e + 4 <= n) {
+        const f4 x = *reinterpret_cast<const f4*>(C.master + e);
+        const uint32_t h[4] = {encode16(x.x, C.param_dt), encode16(x.y, C.param_dt),
+                               encode16(x.z, C.param_dt), encode16(x.w, C.param_dt)};
+        store4_16(p16 + e, h, C.param_align);
+      } else {
+        for (int q = 0; q < 4; ++q)
+          if (e + q < n) p16[e + q] = static_cast<uint16_t>(encode16(C.master[e + q], C.param_dt));
+      }
     }
-    const int64_t j = nv * kVec + tid;
-    if (j < C.n) p16[j] = static_cast<uint16_t>(encode16(C.master[j], C.param_dt));
-  } else {
-    for (int64_t j = tid; j < C.n; j += nthreads)
-      p16[j] = static_cast<uint16_t>(encode16(C.master[j], C.param_dt));
   }
-}
-
-// ------------------------------------------------------------------------
-// Grid sizing: as many blocks as stay resident on the device (occupancy times
-// compute units), no more than the work needs, at most kMaxBlocks.
-// ------------------------------------------------------------------------
-
-int resident_blocks(const void* kernel) {
-  static std::mutex mu;
-  static std::unordered_map<uint64_t, int> cache;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 1024;
-  const uint64_t key = (reinterpret_cast<uint64_t>(kernel) << 8) ^ static_cast<uint64_t>(dev);
-  {
-    std::lock_guard<std::mutex> lk(mu);
-    auto it = cache.find(key);
-    if (it != cache.end()) return it->second;
-  }
-  int cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0) != hipSuccess || per_cu < 1)
-    per_cu = 1;
-  int blocks = cus * per_cu;
-  if (blocks > kMaxBlocks) blocks = kMaxBlocks;
-  if (blocks < 1) blocks = 1;
-  std::lock_guard<std::mutex> lk(mu);
-  cache[key] = blocks;
-  return blocks;
-}
-
-int grid_for(const void* kernel, int64_t n, bool vec) {
-  // threads needed: one per 8-element vector (+ tail) on the vector path,
-  // one per element otherwise
-  const int64_t units = vec ? (n / kVec + ((n % kVec) ? 1 : 0)) : n;
-  int64_t need = (units + kBlock - 1) / kBlock;
-  if (need < 1) need = 1;
-  const int cap = resident_blocks(kernel);
-  return static_cast<int>(need < cap ? need : cap);
 }
 
 template <int SRC, bool VEC, bool CHECKED>
 hipError_t adam_launch(const AdamArgs& a, hipStream_t s) {
-  const void* k = reinterpret_cast<const void*>(&adam_kernel<SRC, VEC, CHECKED>);
-  const int grid = grid_for(k, a.n, VEC);
-  hipLaunchKernelGGL((adam_kernel<SRC, VEC, CHECKED>), dim3(grid), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL((adam_kernel<SRC, VEC, CHECKED>), dim3(stream_grid(a.n)), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
 template <int SRC, bool VEC>
 hipError_t reduce_launch(const ReduceArgs& a, hipStream_t s) {
-  const void* k = reinterpret_cast<const void*>(&reduce_kernel<SRC, VEC>);
-  const int grid = grid_for(k, a.n, VEC);
-  hipLaunchKernelGGL((reduce_kernel<SRC, VEC>), dim3(grid), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL((reduce_kernel<SRC, VEC>), dim3(stream_grid(a.n)), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
@@ -556,8 +474,13 @@ hipError_t launch_reduce(const ReduceArgs& a, int src, bool vec, hipStream_t s) 
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_fold(const FoldArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(fold_kernel, dim3(kFoldBlocks), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(kFinalizeThreads), 0, s, a);
+  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
@@ -572,13 +495,10 @@ hipError_t launch_state_init(zero_step_state* st, float loss_scale, hipStream_t 
 }
 
 hipError_t launch_cast(const CastArgs& a, bool vec, hipStream_t s) {
-  if (vec) {
-    const void* k = reinterpret_cast<const void*>(&cast_kernel<true>);
-    hipLaunchKernelGGL(cast_kernel<true>, dim3(grid_for(k, a.n, true)), dim3(kBlock), 0, s, a);
-  } else {
-    const void* k = reinterpret_cast<const void*>(&cast_kernel<false>);
-    hipLaunchKernelGGL(cast_kernel<false>, dim3(grid_for(k, a.n, false)), dim3(kBlock), 0, s, a);
-  }
+  if (vec)
+    hipLaunchKernelGGL(cast_kernel<true>, dim3(stream_grid(a.n)), dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL(cast_kernel<false>, dim3(stream_grid(a.n)), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 

@@ -9,19 +9,23 @@
 
 namespace zdp {
 
-constexpr int kBlock = 256;          // threads per block in the streaming kernels
-constexpr int kVec = 8;              // elements per thread per iteration (16 B of 16-bit, 32 B of fp32)
-constexpr int kMaxBlocks = 4096;     // partial slots per group
-constexpr int kInlineReplicas = 64;  // replica pointers carried in the kernel arguments
-constexpr size_t kWorkspaceHeader = 256;
+// Streaming layout: a block of 256 threads owns tiles of 4096 consecutive
+// elements; in a tile, lane l of the block handles the 4-element quads
+// l, l + 256, l + 512, l + 768, so each wavefront instruction touches one
+// contiguous run (1 KiB of fp32, 512 B of 16-bit data).
+constexpr int kBlock = 256;
+constexpr int kQuadsPerThread = 4;
+constexpr int kTile = kBlock * kQuadsPerThread * 4;  // elements per tile
+constexpr int kMaxGrid = 1 << 20;                    // blocks per launch (tiles beyond: grid-stride)
+constexpr int kInlineReplicas = 64;                  // replica pointers carried in the kernel arguments
 
-// One block's contribution to the norm and the overflow flag.
-struct Partial {
-  double sumsq;
-  int32_t flag;
-  int32_t pad;
-};
-static_assert(sizeof(Partial) == 16, "partial layout");
+// Workspace: [0, kHeaderBytes) per-group level-2 norm partials, then one fp64
+// partial per block of the last launch (reused launch after launch: the
+// fold that consumes it runs before the next launch in stream order).
+constexpr int kFoldBlocks = 256;                     // level-2 partials per group
+constexpr size_t kHeaderBytes = static_cast<size_t>(ZERO_MAX_GROUPS) * kFoldBlocks * sizeof(double);
+constexpr size_t kScratchBytes = static_cast<size_t>(kMaxGrid) * sizeof(double);
+constexpr size_t kWorkspaceBytes = kHeaderBytes + kScratchBytes;
 
 // Where the averaged gradient of a shard comes from.
 struct GradSource {
@@ -43,14 +47,13 @@ struct AdamArgs {
   float* v;
   void* param;          // flat_param + param_offset (already offset), or null
   int32_t param_dt;     // ZERO_DT_F16 / ZERO_DT_BF16 / 0
-  int32_t param_align;  // 16, 8, 4 or 2: largest power-of-two alignment of param, capped
+  int32_t param_align;  // 8, 4 or 2: largest power-of-two alignment of param, capped at 8
   double beta1_d, beta2_d;
   float lr, beta1, beta2, eps, c1, c2, decay;
   int32_t has_decay;
   int32_t group;
   const zero_step_state* state;
-  Partial* partials;  // slot of this group: kMaxBlocks entries
-  int32_t* count;     // number of blocks that wrote partials for this group
+  double* partials;  // one per block (fused pipeline); null in the checked pipeline
 };
 
 // Arguments of the average kernel (checked pipeline) and of the single-copy scan.
@@ -59,13 +62,19 @@ struct ReduceArgs {
   int64_t n;
   float* avg_out;  // null: scan only
   const zero_step_state* state;
-  Partial* partials;
-  int32_t* count;
+  double* partials;
+};
+
+// Fold one launch's block partials into a group's level-2 partials, in a
+// fixed order (block j of the fold sums a fixed contiguous range).
+struct FoldArgs {
+  const double* partials;
+  int64_t count;
+  double* level2;  // kFoldBlocks entries of the group
 };
 
 struct FinalizeArgs {
-  const Partial* partials;  // base: group g at partials + g * kMaxBlocks
-  const int32_t* counts;
+  const double* level2;  // ZERO_MAX_GROUPS x kFoldBlocks
   zero_step_state* state;
   int32_t n_groups;
   int32_t mode;  // 0: norm + skip verdict only; 1: norm, then commit a static-scale step
@@ -96,10 +105,18 @@ struct CastArgs {
 
 enum SrcKind { kSrcAvg = 0, kSrcF16 = 1, kSrcBF16 = 2 };
 
-// Launchers (kernels.hip). Each returns the hipError_t of the launch.
-// `grid` is chosen by the caller; `vec` selects the 16-byte vector path.
+// Blocks of a streaming launch over n elements.
+inline int stream_grid(int64_t n) {
+  int64_t tiles = (n + kTile - 1) / kTile;
+  if (tiles < 1) tiles = 1;
+  return static_cast<int>(tiles < kMaxGrid ? tiles : kMaxGrid);
+}
+
+// Launchers (kernels.hip). Each returns the hipError_t of its launches.
+// `vec` selects the aligned quad path.
 hipError_t launch_adam(const AdamArgs& a, int src_kind, bool vec, bool checked, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, int src_kind, bool vec, hipStream_t s);
+hipError_t launch_fold(const FoldArgs& a, hipStream_t s);
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
 hipError_t launch_commit(const CommitArgs& a, hipStream_t s);
 hipError_t launch_state_init(zero_step_state* st, float loss_scale, hipStream_t s);
