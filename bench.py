@@ -45,10 +45,24 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    p.add_argument("--cpu-sample", type=int, default=1 << 27,
+    p.add_argument("--cpu-sample", type=int, default=1 << 29,
                    help="elements of the shard the CPU oracle steps once (0: skip)")
     p.add_argument("--quiet", action="store_true")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                   help="only run a plain device copy of BYTES bytes --steps times (to calibrate "
+                        "HBM byte counters against a kernel of known traffic)")
     return p.parse_args()
+
+
+def copy_calibration(args):
+    """A plain copy of known size: BYTES read and BYTES written per launch."""
+    import torch
+    src = torch.ones(args.copy_calibration, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": args.copy_calibration, "launches": args.steps}), flush=True)
 
 
 def log(args, *a):
@@ -157,6 +171,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     wl = WORKLOADS[args.workload]
