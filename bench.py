@@ -159,7 +159,7 @@ def cpu_baseline(setup, sample, args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs the single-rank step on one GPU; --gpus {args.gpus} is not "
+        print(f"bench.py: the partitioned step runs one rank on one GPU; --gpus {args.gpus} is not "
               f"supported (no collectives, no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
     import torch
