@@ -70,13 +70,17 @@ class _State(ctypes.Structure):
 
 
 def lib():
-    """Load liboracle.so, compiling it first if it is missing or stale."""
+    """Load liboracle.so, compiling it first if it is missing or stale.
+    ZDP_ORACLE_LIB names another build of the oracle source to load instead
+    (the mutation tests use it to run the pins against planted mistakes)."""
     global _LIB
     if _LIB is None:
-        path = _build.LIB
-        if (not os.path.exists(path)
-                or os.path.getmtime(path) < os.path.getmtime(_build.SRC)):
-            _build.build()
+        path = os.environ.get("ZDP_ORACLE_LIB")
+        if not path:
+            path = _build.LIB
+            if (not os.path.exists(path)
+                    or os.path.getmtime(path) < os.path.getmtime(_build.SRC)):
+                _build.build()
         L = ctypes.CDLL(path)
         L.oracle_f16_decode.argtypes = [ctypes.c_uint16]
         L.oracle_f16_decode.restype = ctypes.c_float

@@ -154,3 +154,32 @@ def test_group_hyperparameters_apply_per_group():
     a2 = _group(200, 1, "f16", 10, wd=0.1)
     oracle.step([a2], oracle.Policy(), oracle.State())
     np.testing.assert_array_equal(a.master, a2.master)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_loss_scale_is_unscaled_before_the_update(dt):
+    """The loss scale only protects the 16-bit gradients; the step unscales
+    first (DeepSpeed walkthrough §6 step 3), so with a power-of-two scale the
+    update equals the update of the unscaled gradients, bit for bit. Scaling a
+    16-bit value by 2^16 is exact while it stays in range, as here."""
+    n, scale = 4000, 65536.0
+    odt = oracle.F16 if dt == "f16" else oracle.BF16
+    master0 = normal_f32_np(n, 0.02, "ls-master")
+    plain = [grads16_np(n, dt, 1.0, seed=("ls", r)) for r in range(3)]
+    scaled = [to16_bits_np(oracle.decode16(b, odt) * np.float32(scale), dt) for b in plain]
+    for b, s in zip(plain, scaled):  # the scaled copies hold exactly scale x the plain values
+        np.testing.assert_array_equal(oracle.decode16(s, odt), oracle.decode16(b, odt) * np.float32(scale))
+    runs = []
+    for reps, ls in ((plain, 1.0), (scaled, scale)):
+        g = oracle.Group(replicas=reps, grad_dt=odt, master=master0.copy(), m=np.zeros(n, np.float32),
+                         v=np.zeros(n, np.float32), param=np.zeros(n, np.uint16), param_dt=odt,
+                         weight_decay=0.1)
+        st = oracle.State(loss_scale=ls)
+        for _ in range(3):
+            oracle.step([g], oracle.Policy(), st)
+        runs.append((g, st))
+    (a, sa), (b, sb) = runs
+    for x, y in ((a.master, b.master), (a.m, b.m), (a.v, b.v)):
+        np.testing.assert_array_equal(x.view(np.uint32), y.view(np.uint32))
+    np.testing.assert_array_equal(a.param, b.param)
+    assert sa.norm2 == sb.norm2
