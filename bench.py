@@ -105,24 +105,24 @@ class Setup:
             self.shard += n
         self.ws = zdp.new_workspace(len(self.groups))
         self.state = zdp.new_state(wl.loss_scale)
-        self.scaler = zdp.scaler(True) if wl.dynamic_loss_scale else None
+        self.policy = zdp.policy(True) if wl.dynamic_loss_scale else None
         if wl.dynamic_loss_scale:
             self.avg = [torch.empty_like(g.master) for g in self.groups]
 
     def step(self):
         import zero_dp_partitioned_amd as zdp
-        if self.scaler is None:
+        if self.policy is None:
             zdp.adam_step(self.groups, self.ws, self.state)
             return
         # dynamic loss scale: average pass, norm / overflow verdict, checked update
         for gi, g in enumerate(self.groups):
             zdp.reduce_grad_segment(g.replicas, self.avg[gi], self.ws, gi, self.state)
-        zdp.grad_norm_overflow(None, self.ws, len(self.groups), self.state, self.scaler)
+        zdp.grad_norm_overflow(None, self.ws, len(self.groups), self.state, self.policy)
         reps = [g.replicas for g in self.groups]
         for gi, g in enumerate(self.groups):
             g.replicas, g.avg = None, self.avg[gi]
         try:
-            zdp.adam_step(self.groups, self.ws, self.state, self.scaler)
+            zdp.adam_step(self.groups, self.ws, self.state, self.policy)
         finally:
             for gi, g in enumerate(self.groups):
                 g.replicas, g.avg = reps[gi], None

@@ -88,21 +88,30 @@ typedef struct {
   int32_t overflow;     /* last step: 1 if any averaged gradient was inf/NaN   */
   int32_t skipped;      /* last step: 1 if it was voided by the overflow check */
   int32_t good_steps;   /* applied steps since the last loss-scale change      */
-  int32_t reserved;
+  float clip_coef;      /* last step: gradient-clipping multiplier (1 = none)  */
 } zero_step_state;
 
-/* Loss-scale policy. skip_on_overflow = 0: static scale, every step applies
- * (an inf/NaN gradient then propagates into the state). skip_on_overflow = 1:
- * dynamic scale: a step whose averaged gradient holds inf/NaN changes nothing
- * but the scale (S <- max(S * backoff, min_scale)); after growth_interval
- * applied steps in a row, S <- S * growth (growth_interval 0 = never). */
+/* Step policy: loss scaling and gradient clipping.
+ * skip_on_overflow = 0: static scale, every step applies (an inf/NaN gradient
+ *   then propagates into the state).
+ * skip_on_overflow = 1: dynamic scale: a step whose averaged gradient holds
+ *   inf/NaN changes nothing but the scale (S <- max(S * backoff, min_scale));
+ *   after growth_interval applied steps in a row, S <- S * growth
+ *   (growth_interval 0 = never).
+ * max_grad_norm > 0: clip the unscaled gradient to this global norm
+ *   [DeepSpeed walkthrough §6 step 3 "unscale and clip"]: multiplier
+ *   c = min(1, max_norm / (norm + 1e-6)) formed in fp64 and rounded once to
+ *   fp32, g <- (avg * (1/S)) * c; 0 = no clipping.
+ * Skipping and clipping both need the norm before the update, so either one
+ * selects the checked pipeline (see zero_adam_step). */
 typedef struct {
   int32_t skip_on_overflow;
   int32_t growth_interval;
   double backoff;
   double growth;
   double min_scale;
-} zero_scaler;
+  double max_grad_norm;
+} zero_policy;
 
 /* One parameter group's shard for zero_adam_step().
  * Gradient source, exactly one of:
@@ -189,13 +198,15 @@ int zero_reduce_grad_segment(const void* const* replicas, int32_t n_d, int32_t g
  * workspace slot g for each g < n_groups with grads[g] != NULL. Then combine
  * the partials of slots 0 .. n_groups-1 in a fixed order into
  * state->grad_norm_sq / grad_norm (the norm of the unscaled gradient over all
- * groups) and state->overflow, and set state->skipped = overflow &&
- * scaler->skip_on_overflow (scaler may be NULL: no skip). Does not advance
- * the step. `grads` and `counts` are host arrays.
+ * groups) and state->overflow, set state->skipped = overflow &&
+ * policy->skip_on_overflow and state->clip_coef from policy->max_grad_norm
+ * (policy may be NULL: no skip, no clip). When overflow is set the norm is
+ * reported as NaN. Does not advance the step. `grads` and `counts` are host
+ * arrays.
  * Errors: INVALID_ARG, ALIGNMENT, WORKSPACE. */
 int zero_grad_norm_overflow(const void* const* grads, const int64_t* counts, int32_t grad_dt,
                             int32_t n_groups, void* workspace, size_t workspace_bytes,
-                            const zero_scaler* scaler, zero_step_state* state, void* stream);
+                            const zero_policy* policy, zero_step_state* state, void* stream);
 
 /* One Adam/AdamW step over n_groups groups of this rank's shard [reading
  * notes, second part §3; DeepSpeed walkthrough §6 steps 3-5]. With applied
@@ -206,20 +217,22 @@ int zero_grad_norm_overflow(const void* const* grads, const int64_t* counts, int
  *   m = beta1*m + fp32(1-beta1)*g;   v = beta2*v + fp32(1-beta2)*(g*g)
  *   theta -= lr * ((m / b1) / (sqrt(v / b2) + eps))
  *   master = theta;  flat_param[param_offset + j] = RNE16(theta)
- * Pipelines, chosen by the scaler:
- *   - static scale (scaler NULL or skip_on_overflow 0), "fused": one pass per
- *     group reads the gradient source, averages, unscales, updates and writes
- *     back, and emits norm/overflow partials; a final one-block kernel forms
- *     the norm and the flag and advances the step. No
- *     zero_grad_norm_overflow() call is needed.
- *   - dynamic scale (skip_on_overflow 1), "checked": the caller has already run
- *     zero_grad_norm_overflow() on this step's gradients; if it set
- *     state->skipped, nothing but the loss scale changes; otherwise the update
- *     is applied and the step advances. Scale backoff/growth happen here.
+ * Pipelines, chosen by the policy:
+ *   - "fused" (policy NULL, or no skip and no clipping): one pass per group
+ *     reads the gradient source, averages, unscales, updates and writes back,
+ *     and emits norm/overflow partials; a fold and a one-block kernel form the
+ *     norm and the flag and advance the step. No zero_grad_norm_overflow()
+ *     call is needed.
+ *   - "checked" (skip_on_overflow 1 or max_grad_norm > 0): the caller has
+ *     already run zero_grad_norm_overflow() on this step's gradients with the
+ *     same policy; if it set state->skipped, nothing but the loss scale
+ *     changes; otherwise the update is applied with g multiplied by
+ *     state->clip_coef, and the step advances. Scale backoff/growth happen
+ *     here.
  * `groups` is a host array; group g uses workspace slot g and the beta powers
  * state->beta*_pow[g].
  * Errors: INVALID_ARG, ALIGNMENT, WORKSPACE, UNSUPPORTED. */
-int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_scaler* scaler,
+int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_policy* policy,
                    void* workspace, size_t workspace_bytes, zero_step_state* state, void* stream);
 
 /* Copy an fp32 master shard into the 16-bit flat vector [DeepSpeed

@@ -55,6 +55,7 @@ class _Policy(ctypes.Structure):
         ("backoff", ctypes.c_double),
         ("growth", ctypes.c_double),
         ("min_scale", ctypes.c_double),
+        ("max_grad_norm", ctypes.c_double),
     ]
 
 
@@ -66,6 +67,8 @@ class _State(ctypes.Structure):
         ("overflow", ctypes.c_int32),
         ("skipped", ctypes.c_int32),
         ("good_steps", ctypes.c_int32),
+        ("clip", ctypes.c_float),
+        ("pad_", ctypes.c_int32),
     ]
 
 
@@ -103,7 +106,7 @@ def lib():
         L.oracle_norm_overflow.argtypes = [_f32p, ctypes.c_int64, ctypes.c_float,
                                            _f64p, _i32p]
         L.oracle_norm_overflow.restype = None
-        L.oracle_adam_update.argtypes = [ctypes.c_int64, _f32p, ctypes.c_float,
+        L.oracle_adam_update.argtypes = [ctypes.c_int64, _f32p, ctypes.c_float, ctypes.c_float,
                                          _f32p, _f32p, _f32p, _u16p, ctypes.c_int32,
                                          ctypes.c_int64, ctypes.c_double, ctypes.c_double,
                                          ctypes.c_double, ctypes.c_double, ctypes.c_double]
@@ -222,7 +225,7 @@ def inv_scale_of(loss_scale):
 
 
 def adam_update(avg, inv_scale, master, m, v, t, lr, beta1, beta2, eps, weight_decay,
-                param=None, param_dt=F16):
+                param=None, param_dt=F16, clip=1.0):
     """In-place update of master/m/v (and param, a uint16 array) for applied step t."""
     avg = _c(avg, np.float32)
     for a in (master, m, v):
@@ -234,7 +237,7 @@ def adam_update(avg, inv_scale, master, m, v, t, lr, beta1, beta2, eps, weight_d
             raise ValueError("param must be contiguous uint16 of the shard length")
         pp = _ptr(param, ctypes.c_uint16)
     lib().oracle_adam_update(avg.size, _ptr(avg, ctypes.c_float), ctypes.c_float(inv_scale),
-                             _ptr(master, ctypes.c_float), _ptr(m, ctypes.c_float),
+                             ctypes.c_float(clip), _ptr(master, ctypes.c_float), _ptr(m, ctypes.c_float),
                              _ptr(v, ctypes.c_float), pp, param_dt, int(t), lr, beta1,
                              beta2, eps, weight_decay)
 
@@ -250,6 +253,7 @@ class Policy:
     backoff: float = 0.5
     growth: float = 2.0
     min_scale: float = 1.0
+    max_grad_norm: float = 0.0
 
 
 @dataclass
@@ -260,6 +264,7 @@ class State:
     overflow: int = 0
     skipped: int = 0
     good_steps: int = 0
+    clip: float = 1.0
 
     @property
     def grad_norm(self):
@@ -316,12 +321,13 @@ def step(groups, policy, state):
         G[i].lr, G[i].beta1, G[i].beta2 = g.lr, g.beta1, g.beta2
         G[i].eps, G[i].weight_decay = g.eps, g.weight_decay
     P = _Policy(int(policy.skip_on_overflow), int(policy.growth_interval),
-                policy.backoff, policy.growth, policy.min_scale)
+                policy.backoff, policy.growth, policy.min_scale, policy.max_grad_norm)
     S = _State(state.step, state.norm2, state.loss_scale, state.overflow,
-               state.skipped, state.good_steps)
+               state.skipped, state.good_steps, state.clip, 0)
     rc = lib().oracle_step(G, len(groups), ctypes.byref(P), ctypes.byref(S))
     if rc != 0:
         raise RuntimeError(f"oracle_step rc={rc}")
     state.step, state.norm2, state.loss_scale = S.step, S.norm2, S.loss_scale
     state.overflow, state.skipped, state.good_steps = S.overflow, S.skipped, S.good_steps
+    state.clip = S.clip
     return state

@@ -292,8 +292,9 @@ static double beta_pow(double beta, int64_t t)
  * rank's fp32 master/m/v shard, followed by the fp32 -> 16-bit copy into the
  * rank's slice of the flat parameter vector [NOTES §3 update equations;
  * DS12 §6 steps 3-5; PAPER §3.1 for the fp32 state]. `param` points at the
- * first element of the rank's slice (NULL: no writeback). */
-void oracle_adam_update(int64_t n, const float *a, float inv_scale,
+ * first element of the rank's slice (NULL: no writeback). `clip` multiplies
+ * the unscaled gradient (DS12 §6 step 3 unscales and clips; 1 = no clip). */
+void oracle_adam_update(int64_t n, const float *a, float inv_scale, float clip,
                         float *master, float *m, float *v,
                         uint16_t *param, int32_t param_dt, int64_t t,
                         double lr, double beta1, double beta2, double eps,
@@ -308,6 +309,7 @@ void oracle_adam_update(int64_t n, const float *a, float inv_scale,
     const float epsf = (float)eps, lrf = (float)lr;
     for (int64_t j = 0; j < n; ++j) {
         float g = a[j] * inv_scale;              /* unscale */
+        g = g * clip;                            /* clip (1 = none) */
         float theta = master[j];
         if (weight_decay != 0.0)
             theta = theta * decay;               /* decoupled decay */
@@ -358,6 +360,7 @@ typedef struct {
     double backoff;            /* scale factor on overflow, e.g. 0.5               */
     double growth;             /* scale factor after growth_interval good steps    */
     double min_scale;          /* floor of the scale                               */
+    double max_grad_norm;      /* clip the gradient to this global norm (0 = off)  */
 } oracle_policy;
 
 typedef struct {
@@ -367,7 +370,21 @@ typedef struct {
     int32_t overflow;    /* last flag */
     int32_t skipped;     /* last call skipped */
     int32_t good_steps;  /* consecutive applied steps since the last scale change */
+    float clip;          /* last clip multiplier (1 = none) */
+    int32_t pad_;
 } oracle_state;
+
+/* Clip multiplier for a global norm: min(1, max_norm / (norm + 1e-6)) in
+ * fp64, rounded once to fp32; 1 when clipping is off or the norm is not
+ * finite. The pages name clipping (DS12 §6 step 3) without its formula; this
+ * is the usual global-norm rule with torch's 1e-6 guard. */
+static float clip_multiplier(double norm2, double max_norm)
+{
+    if (!(max_norm > 0.0) || !isfinite(norm2))
+        return 1.0f;
+    double c = max_norm / (sqrt(norm2) + 1e-6);
+    return (float)(c < 1.0 ? c : 1.0);
+}
 
 int oracle_step(const oracle_group *groups, int32_t n_groups,
                 const oracle_policy *policy, oracle_state *st)
@@ -394,6 +411,7 @@ int oracle_step(const oracle_group *groups, int32_t n_groups,
     if (rc == OR_OK) {
         st->norm2 = norm2;
         st->overflow = flag;
+        st->clip = clip_multiplier(norm2, policy->max_grad_norm);
         if (flag && policy->skip_on_overflow) {
             double s = (double)st->loss_scale * policy->backoff;
             if (s < policy->min_scale)
@@ -405,7 +423,7 @@ int oracle_step(const oracle_group *groups, int32_t n_groups,
             int64_t t = st->step + 1;
             for (int32_t g = 0; g < n_groups; ++g) {
                 const oracle_group *G = &groups[g];
-                oracle_adam_update(G->n, avg[g], inv_scale, G->master, G->m, G->v,
+                oracle_adam_update(G->n, avg[g], inv_scale, st->clip, G->master, G->m, G->v,
                                    G->param, G->param_dt, t, G->lr, G->beta1,
                                    G->beta2, G->eps, G->weight_decay);
             }

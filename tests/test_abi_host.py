@@ -40,7 +40,7 @@ def test_struct_sizes_match_header_layout():
     assert ctypes.sizeof(zdp.Segment) == 16
     assert ctypes.sizeof(zdp.TensorSlice) == 32
     assert ctypes.sizeof(zdp.StepState) == 168
-    assert ctypes.sizeof(zdp.Scaler) == 32
+    assert ctypes.sizeof(zdp.Policy) == 40
     assert ctypes.sizeof(zdp._Group) == 120
 
 
@@ -131,10 +131,15 @@ def test_device_calls_reject_bad_arguments_before_launch():
     garr = (zdp._Group * 1)(g)
     assert L.zero_adam_step(garr, 1, None, fake, W, fake, None) == zdp.ERR_INVALID_ARG
     assert L.zero_adam_step(garr, 9, None, fake, W, fake, None) == zdp.ERR_INVALID_ARG
-    bad = zdp.scaler(True, backoff=0.0)
+    bad = zdp.policy(True, backoff=0.0)
     g.beta1 = 0.9
     garr = (zdp._Group * 1)(g)
     assert L.zero_adam_step(garr, 1, ctypes.byref(bad), fake, W, fake, None) == zdp.ERR_INVALID_ARG
+    for clip in (-1.0, float("inf"), float("nan")):
+        badclip = zdp.policy(max_grad_norm=clip)
+        assert L.zero_adam_step(garr, 1, ctypes.byref(badclip), fake, W, fake, None) == zdp.ERR_INVALID_ARG
+        assert L.zero_grad_norm_overflow(None, None, 1, 1, fake, W, ctypes.byref(badclip), fake,
+                                         None) == zdp.ERR_INVALID_ARG
     # a workspace smaller than zero_workspace_bytes()
     g.beta1 = 0.9
     garr2 = (zdp._Group * 2)(g, g)

@@ -58,6 +58,7 @@ def _compare_state(tag, st, ost):
     assert s["skipped"] == ost.skipped, tag
     assert s["loss_scale"] == np.float32(ost.loss_scale), tag
     assert s["good_steps"] == ost.good_steps, tag
+    assert s["clip_coef"] == np.float32(ost.clip), tag
     if np.isfinite(ost.norm2):
         assert abs(s["grad_norm_sq"] - ost.norm2) <= NORM_RTOL * ost.norm2, (tag, s["grad_norm_sq"], ost.norm2)
         assert s["grad_norm"] == pytest.approx(np.sqrt(ost.norm2), rel=1e-6)
@@ -175,7 +176,7 @@ def test_checked_pipeline_skip_and_scale(n, n_d, dt, use_avg):
     print(f"[case] {tag}", flush=True)
     odt = ORACLE_DT[dt]
     pol = oracle.Policy(skip_on_overflow=True, growth_interval=2)
-    sc = zdp.scaler(True, growth_interval=2)
+    sc = zdp.policy(True, growth_interval=2)
     master0 = normal_f32_np(n, 0.02, (7, "master"))
     flat0 = to16_bits_np(normal_f32_np(n + 11, 0.02, (7, "flat")), dt)
     off = 11
@@ -215,7 +216,7 @@ def test_checked_single_copy_prepass_two_groups():
     odt = ORACLE_DT[dt]
     sizes, wds = (30_011, 513), (0.1, 0.0)
     pol = oracle.Policy(skip_on_overflow=True, growth_interval=1000)
-    sc = zdp.scaler(True)
+    sc = zdp.policy(True)
     dev_groups, ogs, flats = [], [], []
     for i, (n, wd) in enumerate(zip(sizes, wds)):
         master0 = normal_f32_np(n, 0.02, (8, i, "master"))
@@ -336,3 +337,60 @@ def test_determinism_run_to_run():
         outs.append([down32(master), down32(m), down32(v), down16(flat), st.cpu().numpy()])
     for a, b in zip(*outs):
         np.testing.assert_array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+# --------------------------------------------------------------------------
+# gradient clipping by the global norm (checked pipeline)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,n_d,dt,skip,max_norm,scale", [
+    (60_001, 4, "f16", False, 0.02, 1.0),      # static scale, always clipped
+    (60_001, 4, "bf16", False, 1e3, 1.0),      # threshold far above the norm: a no-op
+    (30_011, 8, "f16", True, 0.01, 65536.0),   # dynamic scale + clipping, one overflow
+    (30_011, 1, "bf16", True, 0.01, 1024.0),   # single copy: the norm pass scans it directly
+])
+def test_checked_pipeline_with_clipping(n, n_d, dt, skip, max_norm, scale):
+    tag = f"clip n={n} n_d={n_d} {dt} skip={skip} max={max_norm}"
+    print(f"[case] {tag}", flush=True)
+    odt = ORACLE_DT[dt]
+    pol = oracle.Policy(skip_on_overflow=skip, growth_interval=1000, max_grad_norm=max_norm)
+    sc = zdp.policy(skip, growth_interval=1000, max_grad_norm=max_norm)
+    master0 = normal_f32_np(n, 0.02, (13, "master"))
+    flat0 = to16_bits_np(master0, dt)
+    master, m, v = up32(master0), torch.zeros(n, device=DEV), torch.zeros(n, device=DEV)
+    avg = torch.empty(n, dtype=torch.float32, device=DEV)
+    flat = up16(flat0, dt)
+    ws, st = zdp.new_workspace(1), zdp.new_state(scale)
+    og = oracle.Group(replicas=None, grad_dt=odt, master=master0.copy(), m=np.zeros(n, np.float32),
+                      v=np.zeros(n, np.float32), param=flat0.copy(), param_dt=odt, weight_decay=0.1)
+    ost = oracle.State(loss_scale=scale)
+    clipped = 0
+    for k in range(5):
+        reps = [grads16_np(n, dt, ost.loss_scale, (13, "g", k, r)) for r in range(n_d)]
+        if skip and k == 2:
+            reps[0] = reps[0].copy()
+            reps[0][n - 1] = POS_INF[dt]
+        dreps = [up16(r, dt) for r in reps]
+        if n_d == 1:
+            zdp.grad_norm_overflow(dreps, ws, 1, st, sc)
+            grp = zdp.Group(master, m, v, replicas=dreps, flat_param=flat, weight_decay=0.1)
+        else:
+            zdp.reduce_grad_segment(dreps, avg, ws, 0, st)
+            zdp.grad_norm_overflow(None, ws, 1, st, sc)
+            grp = zdp.Group(master, m, v, avg=avg, flat_param=flat, weight_decay=0.1)
+        zdp.adam_step([grp], ws, st, sc)
+        og.replicas = reps
+        oracle.step([og], pol, ost)
+        torch.cuda.synchronize()
+        _compare_group(f"{tag} call {k + 1}", master, m, v, og)
+        _compare_state(f"{tag} call {k + 1}", st, ost)
+        clipped += ost.clip < 1.0
+    assert_u16_equal(down16(flat), og.param, tag + " param")
+    if max_norm < 1:
+        assert clipped >= 4
+    else:
+        assert clipped == 0
+
+
+def test_fused_pipeline_reports_no_clip():
+    run_fused(5000, 2, "bf16", steps=2, seed=14)

@@ -120,7 +120,7 @@ class Run:
         self.state = zdp.new_state(wl.loss_scale)
         self.ostate = oracle.State(loss_scale=wl.loss_scale)
         self.policy = oracle.Policy(skip_on_overflow=wl.dynamic_loss_scale)
-        self.scaler = zdp.scaler(True) if wl.dynamic_loss_scale else None
+        self.policy_ = zdp.policy(True) if wl.dynamic_loss_scale else None
         self.avg = [torch.empty_like(g.master) for g in self.groups] if wl.dynamic_loss_scale else None
 
     def draw_grads(self, call):
@@ -139,17 +139,17 @@ class Run:
         return False
 
     def gpu_step(self):
-        if self.scaler is None:
+        if self.policy_ is None:
             zdp.adam_step(self.groups, self.ws, self.state)
             return
         for gi, g in enumerate(self.groups):
             zdp.reduce_grad_segment(g.replicas, self.avg[gi], self.ws, gi, self.state)
-        zdp.grad_norm_overflow(None, self.ws, len(self.groups), self.state, self.scaler)
+        zdp.grad_norm_overflow(None, self.ws, len(self.groups), self.state, self.policy_)
         saved = [g.replicas for g in self.groups]
         for gi, g in enumerate(self.groups):
             g.replicas, g.avg = None, self.avg[gi]
         try:
-            zdp.adam_step(self.groups, self.ws, self.state, self.scaler)
+            zdp.adam_step(self.groups, self.ws, self.state, self.policy_)
         finally:
             for gi, g in enumerate(self.groups):
                 g.replicas, g.avg = saved[gi], None

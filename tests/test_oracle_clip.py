@@ -1,0 +1,85 @@
+"""Gradient clipping by the global norm in the oracle.
+
+The DeepSpeed walkthrough (§6 step 3) unscales and clips the rank's gradient
+shard before the update, with the norm of step 2, but gives no formula. The
+reading: multiplier c = min(1, max_norm / (norm + 1e-6)), formed in fp64 and
+rounded once, applied to the unscaled gradient. Pins: torch's
+clip_grad_norm_ followed by torch.optim.Adam/AdamW, both in float64 (an
+independent implementation of the same rule); bit-identity with the unclipped
+step when the norm is below the threshold; the clipped gradient's norm equals
+the threshold."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import grads16_np, normal_f32_np
+
+U = 2.0 ** -24
+LR, B1, B2, EPS = 1e-3, 0.9, 0.999, 1e-8
+
+
+def _group(n, n_d, seed, wd=0.0, scale=1.0):
+    reps = [grads16_np(n, "bf16", scale, seed=(seed, r)) for r in range(n_d)]
+    return oracle.Group(replicas=reps, grad_dt=oracle.BF16, master=normal_f32_np(n, 0.02, (seed, "m")),
+                        m=np.zeros(n, np.float32), v=np.zeros(n, np.float32), weight_decay=wd)
+
+
+@pytest.mark.parametrize("wd", [0.0, 0.1])
+@pytest.mark.parametrize("max_norm", [0.01, 0.03])
+def test_clip_matches_torch_float64(wd, max_norm):
+    n, steps, scale = 5000, 4, 1024.0
+    g = _group(n, 2, 1, wd=wd, scale=scale)
+    p = torch.nn.Parameter(torch.from_numpy(g.master.astype(np.float64)))
+    cls = torch.optim.AdamW if wd else torch.optim.Adam
+    opt = cls([p], lr=LR, betas=(B1, B2), eps=EPS, weight_decay=wd, foreach=False)
+    st = oracle.State(loss_scale=scale)
+    pol = oracle.Policy(max_grad_norm=max_norm)
+    clipped = 0
+    for k in range(steps):
+        g.replicas = [grads16_np(n, "bf16", scale, seed=(1, k, r)) for r in range(2)]
+        a = oracle.average(g.replicas, oracle.BF16)
+        grad = (a.astype(np.float64) / scale)   # exact: power-of-two scale
+        p.grad = torch.from_numpy(grad.copy())
+        total = torch.nn.utils.clip_grad_norm_([p], max_norm)
+        opt.step()
+        oracle.step([g], pol, st)
+        assert np.sqrt(st.norm2) == pytest.approx(float(total), rel=1e-12)
+        clipped += st.clip < 1.0
+    assert clipped == steps  # the gradient norm (~0.05) is above both thresholds
+    want = p.detach().numpy()
+    assert (np.abs(g.master - want) <= steps * (2 * U * np.abs(want) + LR * 32 * U)).all()
+    m_ref = opt.state[p]["exp_avg"].numpy()
+    assert (np.abs(g.m - m_ref) <= 8 * steps * U * np.abs(m_ref).max()).all()
+
+
+def test_clip_is_a_no_op_below_the_threshold():
+    a, b = _group(3000, 4, 2), _group(3000, 4, 2)
+    sa, sb = oracle.State(), oracle.State()
+    oracle.step([a], oracle.Policy(), sa)
+    oracle.step([b], oracle.Policy(max_grad_norm=1e6), sb)
+    assert sb.clip == 1.0
+    for x, y in ((a.master, b.master), (a.m, b.m), (a.v, b.v)):
+        np.testing.assert_array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
+def test_clipped_gradient_has_the_threshold_norm():
+    g = _group(20_000, 2, 3)
+    st = oracle.State()
+    oracle.step([g], oracle.Policy(max_grad_norm=0.02), st)
+    norm = np.sqrt(st.norm2)
+    assert norm > 0.02 and st.clip < 1
+    # m after one step is (1 - beta1) * clip * g exactly up to rounding
+    a = oracle.average(g.replicas, oracle.BF16).astype(np.float64)
+    clipped = a * np.float64(st.clip)
+    assert np.sqrt((clipped ** 2).sum()) == pytest.approx(0.02 * norm / (norm + 1e-6), rel=1e-6)
+    np.testing.assert_allclose(g.m, (1 - B1) * clipped, rtol=4 * U, atol=1e-30)
+
+
+def test_clip_ignored_on_overflow_and_in_skip():
+    g = _group(100, 1, 4)
+    g.replicas[0] = g.replicas[0].copy()
+    g.replicas[0][7] = 0x7F80
+    st = oracle.State()
+    oracle.step([g], oracle.Policy(skip_on_overflow=True, max_grad_norm=0.01), st)
+    assert st.skipped == 1 and st.clip == 1.0

@@ -17,7 +17,7 @@ from oracle import build as oracle_build
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PINS = ["tests/test_oracle_encodings.py", "tests/test_oracle_partition.py",
         "tests/test_oracle_average_norm.py", "tests/test_oracle_adam.py",
-        "tests/test_oracle_step.py"]
+        "tests/test_oracle_step.py", "tests/test_oracle_clip.py"]
 
 MUTATIONS = [
     ("first-moment bias correction dropped", "float mhat = mt / b1;", "float mhat = mt;"),
@@ -53,6 +53,9 @@ MUTATIONS = [
     ("fp16 decode exponent bias off by one", "mag = ldexpf((float)(frac + 1024), e - 25);",
      "mag = ldexpf((float)(frac + 1024), e - 24);"),
     ("tensor slice begins at the shard start", "tensor_begin[count] = ob - b;", "tensor_begin[count] = 0;"),
+    ("clip multiplier not applied", "g = g * clip;                            /* clip (1 = none) */", "(void)clip;"),
+    ("clip from the squared norm", "double c = max_norm / (sqrt(norm2) + 1e-6);", "double c = max_norm / (norm2 + 1e-6);"),
+    ("clip allowed to scale up", "return (float)(c < 1.0 ? c : 1.0);", "return (float)c;"),
 ]
 
 

@@ -55,13 +55,13 @@ class StepState(ctypes.Structure):
                 ("overflow", ctypes.c_int32),
                 ("skipped", ctypes.c_int32),
                 ("good_steps", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("clip_coef", ctypes.c_float)]
 
 
-class Scaler(ctypes.Structure):
+class Policy(ctypes.Structure):
     _fields_ = [("skip_on_overflow", ctypes.c_int32), ("growth_interval", ctypes.c_int32),
                 ("backoff", ctypes.c_double), ("growth", ctypes.c_double),
-                ("min_scale", ctypes.c_double)]
+                ("min_scale", ctypes.c_double), ("max_grad_norm", ctypes.c_double)]
 
 
 class _Group(ctypes.Structure):
@@ -104,8 +104,8 @@ def load():
         sz = ctypes.c_size_t
         L.zero_reduce_grad_segment.argtypes = [ctypes.POINTER(vp), i32, i32, i64, vp, vp, sz, i32, vp, vp]
         L.zero_grad_norm_overflow.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(i64), i32, i32, vp, sz,
-                                              ctypes.POINTER(Scaler), vp, vp]
-        L.zero_adam_step.argtypes = [ctypes.POINTER(_Group), i32, ctypes.POINTER(Scaler), vp, sz, vp, vp]
+                                              ctypes.POINTER(Policy), vp, vp]
+        L.zero_adam_step.argtypes = [ctypes.POINTER(_Group), i32, ctypes.POINTER(Policy), vp, sz, vp, vp]
         L.zero_cast_writeback.argtypes = [vp, i64, vp, i64, i32, vp]
         for name in EXPORTS:
             fn = getattr(L, name)
@@ -206,7 +206,8 @@ def read_state(state):
     s = StepState.from_buffer_copy(raw)
     return {"beta1_pow": list(s.beta1_pow), "beta2_pow": list(s.beta2_pow),
             "grad_norm_sq": s.grad_norm_sq, "grad_norm": s.grad_norm, "loss_scale": s.loss_scale,
-            "step": s.step, "overflow": s.overflow, "skipped": s.skipped, "good_steps": s.good_steps}
+            "step": s.step, "overflow": s.overflow, "skipped": s.skipped, "good_steps": s.good_steps,
+            "clip_coef": s.clip_coef}
 
 
 def new_workspace(n_groups, device="cuda"):
@@ -218,9 +219,16 @@ def new_workspace(n_groups, device="cuda"):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def scaler(skip_on_overflow=False, growth_interval=1000, backoff=0.5, growth=2.0, min_scale=1.0):
-    return Scaler(int(bool(skip_on_overflow)), int(growth_interval), float(backoff), float(growth),
-                  float(min_scale))
+def policy(skip_on_overflow=False, growth_interval=1000, backoff=0.5, growth=2.0, min_scale=1.0,
+           max_grad_norm=0.0):
+    """Loss-scale and clipping policy. Skipping or clipping selects the checked
+    pipeline: reduce_grad_segment / grad_norm_overflow before adam_step."""
+    return Policy(int(bool(skip_on_overflow)), int(growth_interval), float(backoff), float(growth),
+                  float(min_scale), float(max_grad_norm))
+
+
+def is_checked(policy_):
+    return policy_ is not None and (policy_.skip_on_overflow or policy_.max_grad_norm > 0)
 
 
 def reduce_grad_segment(replicas, avg_out, workspace, group, state, stream=None):
@@ -235,7 +243,7 @@ def reduce_grad_segment(replicas, avg_out, workspace, group, state, stream=None)
                                            _stream(stream)))
 
 
-def grad_norm_overflow(grads, workspace, n_groups, state, scaler_=None, stream=None, grad_dtype=None):
+def grad_norm_overflow(grads, workspace, n_groups, state, policy_=None, stream=None, grad_dtype=None):
     """Finalise the norm / overflow flag. ``grads``: None, or a list of n_groups
     entries (a 16-bit tensor to scan, or None for a slot already filled)."""
     if grads is None:
@@ -249,7 +257,7 @@ def grad_norm_overflow(grads, workspace, n_groups, state, scaler_=None, stream=N
             (g.data_ptr() or workspace.data_ptr()) if g is not None else 0 for g in grads])
         cp = (ctypes.c_int64 * n_groups)(*[g.numel() if g is not None else 0 for g in grads])
         dt = _dt(next(g for g in grads if g is not None))
-    sc = ctypes.byref(scaler_) if scaler_ is not None else None
+    sc = ctypes.byref(policy_) if policy_ is not None else None
     _check(load().zero_grad_norm_overflow(gp, cp, dt, n_groups, _ptr(workspace), _nbytes(workspace), sc,
                                           _ptr(state), _stream(stream)))
 
@@ -307,10 +315,10 @@ def _group_struct(g, keep):
     return s
 
 
-def adam_step(groups, workspace, state, scaler_=None, stream=None):
+def adam_step(groups, workspace, state, policy_=None, stream=None):
     keep = []
     arr = (_Group * len(groups))(*[_group_struct(g, keep) for g in groups])
-    sc = ctypes.byref(scaler_) if scaler_ is not None else None
+    sc = ctypes.byref(policy_) if policy_ is not None else None
     _check(load().zero_adam_step(arr, len(groups), sc, _ptr(workspace), _nbytes(workspace), _ptr(state),
                                  _stream(stream)))
 

@@ -84,6 +84,16 @@ int check_workspace(const void* ws, size_t have) {
   return ZERO_OK;
 }
 
+int check_policy(const zero_policy* p) {
+  if (!p) return ZERO_OK;
+  if (!(p->max_grad_norm >= 0.0) || p->max_grad_norm == __builtin_inf())
+    return fail(ZERO_ERR_INVALID_ARG, "max_grad_norm must be finite and >= 0");
+  if (p->skip_on_overflow && (!(p->backoff > 0.0) || !(p->growth >= 1.0) || !(p->min_scale > 0.0) ||
+                              p->growth_interval < 0))
+    return fail(ZERO_ERR_INVALID_ARG, "bad loss-scale policy");
+  return ZERO_OK;
+}
+
 bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
 // Fill a GradSource from a host array of replica pointers. Sets *vec_ok to
@@ -243,11 +253,12 @@ int zero_reduce_grad_segment(const void* const* replicas, int32_t n_d, int32_t g
 
 int zero_grad_norm_overflow(const void* const* grads, const int64_t* counts, int32_t grad_dt,
                             int32_t n_groups, void* workspace, size_t workspace_bytes,
-                            const zero_scaler* scaler, zero_step_state* state, void* stream) {
+                            const zero_policy* policy, zero_step_state* state, void* stream) {
   if (n_groups < 1 || n_groups > ZERO_MAX_GROUPS)
     return fail(ZERO_ERR_INVALID_ARG, "n_groups = %d out of [1, %d]", n_groups, ZERO_MAX_GROUPS);
   if (!state) return fail(ZERO_ERR_INVALID_ARG, "state is NULL");
   if (int rc = check_workspace(workspace, workspace_bytes)) return rc;
+  if (int rc = check_policy(policy)) return rc;
   ReduceArgs R[ZERO_MAX_GROUPS];
   bool vec[ZERO_MAX_GROUPS] = {};
   bool scan[ZERO_MAX_GROUPS] = {};
@@ -282,12 +293,13 @@ int zero_grad_norm_overflow(const void* const* grads, const int64_t* counts, int
   F.state = state;
   F.n_groups = n_groups;
   F.mode = 0;
-  F.skip_on_overflow = scaler ? (scaler->skip_on_overflow != 0) : 0;
+  F.skip_on_overflow = policy ? (policy->skip_on_overflow != 0) : 0;
+  F.max_grad_norm = policy ? policy->max_grad_norm : 0.0;
   hipError_t e = launch_finalize(F, s);
   return e == hipSuccess ? ZERO_OK : hip_fail(e, "finalize launch");
 }
 
-int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_scaler* scaler,
+int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_policy* policy,
                    void* workspace, size_t workspace_bytes, zero_step_state* state, void* stream) {
   if (!groups) return fail(ZERO_ERR_INVALID_ARG, "groups is NULL");
   if (n_groups < 1 || n_groups > ZERO_MAX_GROUPS)
@@ -295,12 +307,9 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_scaler
   if (!state) return fail(ZERO_ERR_INVALID_ARG, "state is NULL");
   if (!aligned(state, 8)) return fail(ZERO_ERR_ALIGNMENT, "state is not 8-byte aligned");
   if (int rc = check_workspace(workspace, workspace_bytes)) return rc;
-  const bool dynamic = scaler && scaler->skip_on_overflow;
-  if (dynamic) {
-    if (!(scaler->backoff > 0.0) || !(scaler->growth >= 1.0) || !(scaler->min_scale > 0.0) ||
-        scaler->growth_interval < 0)
-      return fail(ZERO_ERR_INVALID_ARG, "bad loss-scale policy");
-  }
+  if (int rc = check_policy(policy)) return rc;
+  const bool dynamic = policy && policy->skip_on_overflow;
+  const bool checked = policy && (policy->skip_on_overflow || policy->max_grad_norm > 0.0);
   AdamArgs A[ZERO_MAX_GROUPS];
   int src[ZERO_MAX_GROUPS];
   bool vec[ZERO_MAX_GROUPS];
@@ -355,20 +364,20 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_scaler
     a.has_decay = G.weight_decay != 0.0;
     a.group = g;
     a.state = state;
-    a.partials = dynamic ? nullptr : scratch_of(workspace);
+    a.partials = checked ? nullptr : scratch_of(workspace);
     vec[g] = v;
   }
   if (int rc = check_device()) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   for (int32_t g = 0; g < n_groups; ++g) {
-    hipError_t e = launch_adam(A[g], src[g], vec[g], dynamic, s);
+    hipError_t e = launch_adam(A[g], src[g], vec[g], checked, s);
     if (e != hipSuccess) return hip_fail(e, "update launch");
-    if (!dynamic) {
+    if (!checked) {
       e = fold_into(workspace, g, A[g].n, s);
       if (e != hipSuccess) return hip_fail(e, "fold launch");
     }
   }
-  if (!dynamic) {
+  if (!checked) {
     FinalizeArgs F;
     memset(&F, 0, sizeof F);
     F.level2 = level2_of(workspace, 0);
@@ -386,11 +395,11 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_scaler
   memset(&C, 0, sizeof C);
   C.state = state;
   C.n_groups = n_groups;
-  C.dynamic = 1;
-  C.growth_interval = scaler->growth_interval;
-  C.backoff = scaler->backoff;
-  C.growth = scaler->growth;
-  C.min_scale = scaler->min_scale;
+  C.dynamic = dynamic ? 1 : 0;
+  C.growth_interval = policy->growth_interval;
+  C.backoff = policy->backoff;
+  C.growth = policy->growth;
+  C.min_scale = policy->min_scale;
   for (int32_t g = 0; g < n_groups; ++g) {
     C.beta1[g] = groups[g].beta1;
     C.beta2[g] = groups[g].beta2;

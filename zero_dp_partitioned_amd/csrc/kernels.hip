@@ -144,7 +144,7 @@ __device__ __forceinline__ float source1(const GradSource& S, int64_t j) {
 // ------------------------------------------------------------------------
 
 struct Scalars {
-  float inv_scale, b1, b2, beta1, beta2, c1, c2, eps, lr, decay;
+  float inv_scale, clip, b1, b2, beta1, beta2, c1, c2, eps, lr, decay;
   bool has_decay;
 };
 
@@ -152,6 +152,7 @@ __device__ __forceinline__ Scalars load_scalars(const AdamArgs& A) {
   const zero_step_state* st = A.state;
   Scalars s;
   s.inv_scale = static_cast<float>(1.0 / static_cast<double>(st->loss_scale));
+  s.clip = st->clip_coef;  // set by the norm pass of the checked pipeline; 1 = none
   // beta^t of the step being applied: the stored beta^(t-1) times beta, in fp64
   s.b1 = static_cast<float>(1.0 - st->beta1_pow[A.group] * A.beta1_d);
   s.b2 = static_cast<float>(1.0 - st->beta2_pow[A.group] * A.beta2_d);
@@ -235,8 +236,9 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs A) {
 
   auto one = [&](int64_t j) {
     const float a = source1<SRC>(A.src, j);
-    const float g = a * s.inv_scale;
+    float g = a * s.inv_scale;
     if constexpr (!CHECKED) account(a, g, sumsq, bad);
+    if constexpr (CHECKED) g = g * s.clip;
     float th = A.master[j], m = A.m[j], v = A.v[j];
     adam1(g, th, m, v, s);
     A.master[j] = th;
@@ -260,8 +262,9 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs A) {
         float vv[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float g = a[q] * s.inv_scale;
+          float g = a[q] * s.inv_scale;
           if constexpr (!CHECKED) account(a[q], g, sumsq, bad);
+          if constexpr (CHECKED) g = g * s.clip;
           adam1(g, th[q], mm[q], vv[q], s);
         }
         *reinterpret_cast<f4*>(A.master + e) = (f4){th[0], th[1], th[2], th[3]};
@@ -362,6 +365,7 @@ __global__ void __launch_bounds__(kBlock) finalize_kernel(const FinalizeArgs F) 
   st->overflow = flag;
   if (F.mode == 1) {
     // static loss scale: the update was applied whatever the flag says
+    st->clip_coef = 1.0f;
     st->skipped = 0;
     st->step = st->step + 1;
     for (int g = 0; g < F.n_groups; ++g) {
@@ -370,6 +374,13 @@ __global__ void __launch_bounds__(kBlock) finalize_kernel(const FinalizeArgs F) 
     }
   } else {
     st->skipped = (flag && F.skip_on_overflow) ? 1 : 0;
+    // clip multiplier min(1, max_norm / (norm + 1e-6)), fp64, rounded once
+    float clip = 1.0f;
+    if (F.max_grad_norm > 0.0 && __builtin_isfinite(total)) {
+      const double c = F.max_grad_norm / (__builtin_sqrt(total) + 1e-6);
+      clip = static_cast<float>(c < 1.0 ? c : 1.0);
+    }
+    st->clip_coef = clip;
   }
 }
 
@@ -410,7 +421,7 @@ __global__ void state_init_kernel(zero_step_state* st, float loss_scale) {
   st->overflow = 0;
   st->skipped = 0;
   st->good_steps = 0;
-  st->reserved = 0;
+  st->clip_coef = 1.0f;
 }
 
 // ------------------------------------------------------------------------

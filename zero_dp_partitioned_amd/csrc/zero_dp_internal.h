@@ -77,9 +77,10 @@ struct FinalizeArgs {
   const double* level2;  // ZERO_MAX_GROUPS x kFoldBlocks
   zero_step_state* state;
   int32_t n_groups;
-  int32_t mode;  // 0: norm + skip verdict only; 1: norm, then commit a static-scale step
+  int32_t mode;  // 0: norm, skip verdict, clip multiplier; 1: norm, then commit a static-scale step
   int32_t skip_on_overflow;
   int32_t pad;
+  double max_grad_norm;  // mode 0: clip threshold (0 = none)
   double beta1[ZERO_MAX_GROUPS];
   double beta2[ZERO_MAX_GROUPS];
 };
