@@ -47,6 +47,9 @@ def parse():
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--cpu-sample", type=int, default=1 << 29,
                    help="elements of the shard the CPU oracle steps once (0: skip)")
+    p.add_argument("--pipeline", choices=["checked", "optimistic"], default="checked",
+                   help="dynamic-loss-scale workloads: verdict before the update (checked) or an "
+                        "update into a second state set committed afterwards (optimistic)")
     p.add_argument("--quiet", action="store_true")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="only run a plain device copy of BYTES bytes --steps times (to calibrate "
@@ -75,7 +78,7 @@ class Setup:
     the N_d 16-bit gradient copies of the shard (one buffer, 64-element padded
     stride), and the group's whole 16-bit flat parameter vector."""
 
-    def __init__(self, wl, dev):
+    def __init__(self, wl, dev, optimistic=False):
         import torch
         import zero_dp_partitioned_amd as zdp
         from workloads import derive_seed, fill_normal_, torch_dtype
@@ -98,21 +101,26 @@ class Setup:
             reps = [gbuf[r * stride:r * stride + n] for r in range(wl.n_d)]
             for r, t in enumerate(reps):
                 fill_normal_(t, 1e-3, derive_seed(wl.key, gi, "grad", 0, r), scale=wl.loss_scale)
+            alt = {}
+            if optimistic and wl.dynamic_loss_scale:
+                alt = dict(master_alt=torch.empty_like(master), exp_avg_alt=torch.empty_like(master),
+                           exp_avg_sq_alt=torch.empty_like(master))
             self.groups.append(zdp.Group(
                 master=master, exp_avg=torch.zeros_like(master), exp_avg_sq=torch.zeros_like(master),
                 replicas=reps, flat_param=flat, param_offset=off, lr=wl.lr, beta1=wl.beta1,
-                beta2=wl.beta2, eps=wl.eps, weight_decay=spec.weight_decay))
+                beta2=wl.beta2, eps=wl.eps, weight_decay=spec.weight_decay, **alt))
             self.shard += n
         self.ws = zdp.new_workspace(len(self.groups))
         self.state = zdp.new_state(wl.loss_scale)
-        self.policy = zdp.policy(True) if wl.dynamic_loss_scale else None
-        if wl.dynamic_loss_scale:
+        self.optimistic = optimistic and wl.dynamic_loss_scale
+        self.policy = zdp.policy(True, optimistic=self.optimistic) if wl.dynamic_loss_scale else None
+        if wl.dynamic_loss_scale and not self.optimistic:
             self.avg = [torch.empty_like(g.master) for g in self.groups]
 
     def step(self):
         import zero_dp_partitioned_amd as zdp
-        if self.policy is None:
-            zdp.adam_step(self.groups, self.ws, self.state)
+        if self.policy is None or self.optimistic:
+            zdp.adam_step(self.groups, self.ws, self.state, self.policy)
             return
         # dynamic loss scale: average pass, norm / overflow verdict, checked update
         for gi, g in enumerate(self.groups):
@@ -178,7 +186,7 @@ def main():
     torch.cuda.set_device(dev)
     wl = WORKLOADS[args.workload]
     log(args, f"workload {wl.key}: {wl.title}")
-    setup = Setup(wl, dev)
+    setup = Setup(wl, dev, optimistic=args.pipeline == "optimistic")
     S = setup.shard
     bpp = bytes_per_param(wl.n_d)
     log(args, f"shard {S} params, {len(setup.groups)} group(s), {bpp} B/param, "
@@ -231,6 +239,8 @@ def main():
         "config": {"workload": wl.key, "shard_params": S, "n_d": wl.n_d, "rank": wl.rank,
                    "groups": len(setup.groups), "grad_dtype": wl.grad_dt, "param_dtype": wl.param_dt,
                    "loss_scale": wl.loss_scale, "dynamic_loss_scale": wl.dynamic_loss_scale,
+                   "pipeline": ("optimistic" if setup.optimistic else "checked") if wl.dynamic_loss_scale
+                   else "fused",
                    "bytes_per_param": bpp},
         "gbps": achieved,
         "pct_peak": 100.0 * achieved / PEAK_HBM_GBPS,

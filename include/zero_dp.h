@@ -89,6 +89,9 @@ typedef struct {
   int32_t skipped;      /* last step: 1 if it was voided by the overflow check */
   int32_t good_steps;   /* applied steps since the last loss-scale change      */
   float clip_coef;      /* last step: gradient-clipping multiplier (1 = none)  */
+  int32_t cur;          /* optimistic pipeline: 0 = master/exp_avg/exp_avg_sq
+                           hold the current state, 1 = the *_alt arrays do    */
+  int32_t reserved;
 } zero_step_state;
 
 /* Step policy: loss scaling and gradient clipping.
@@ -102,11 +105,16 @@ typedef struct {
  *   [DeepSpeed walkthrough §6 step 3 "unscale and clip"]: multiplier
  *   c = min(1, max_norm / (norm + 1e-6)) formed in fp64 and rounded once to
  *   fp32, g <- (avg * (1/S)) * c; 0 = no clipping.
- * Skipping and clipping both need the norm before the update, so either one
- * selects the checked pipeline (see zero_adam_step). */
+ * optimistic = 1 (with skip_on_overflow = 1, without clipping): instead of
+ *   waiting for the overflow verdict, update into a second state set and
+ *   commit or discard it afterwards (see zero_adam_step).
+ * Skipping or clipping without `optimistic` needs the norm before the update
+ * and selects the checked pipeline. */
 typedef struct {
   int32_t skip_on_overflow;
   int32_t growth_interval;
+  int32_t optimistic;
+  int32_t reserved;
   double backoff;
   double growth;
   double min_scale;
@@ -120,6 +128,8 @@ typedef struct {
  *             average is formed in the kernel (fused mode), or
  *   avg:      device fp32 [n] average written by zero_reduce_grad_segment().
  * State: master, exp_avg (m), exp_avg_sq (v): device fp32 [n], updated in place.
+ *   The optimistic pipeline also needs master_alt, exp_avg_alt, exp_avg_sq_alt
+ *   (fp32 [n], contents ignored until first written); NULL otherwise.
  * Writeback: flat_param (device, param_dt elements) receives the updated master
  *   rounded to 16 bits at elements [param_offset, param_offset + n); NULL skips
  *   it. Any 2-byte alignment of flat_param + param_offset is accepted.
@@ -134,6 +144,9 @@ typedef struct {
   float* master;
   float* exp_avg;
   float* exp_avg_sq;
+  float* master_alt;
+  float* exp_avg_alt;
+  float* exp_avg_sq_alt;
   void* flat_param;
   int64_t param_offset;
   int32_t param_dt;
@@ -223,12 +236,22 @@ int zero_grad_norm_overflow(const void* const* grads, const int64_t* counts, int
  *     and emits norm/overflow partials; a fold and a one-block kernel form the
  *     norm and the flag and advance the step. No zero_grad_norm_overflow()
  *     call is needed.
- *   - "checked" (skip_on_overflow 1 or max_grad_norm > 0): the caller has
- *     already run zero_grad_norm_overflow() on this step's gradients with the
- *     same policy; if it set state->skipped, nothing but the loss scale
- *     changes; otherwise the update is applied with g multiplied by
- *     state->clip_coef, and the step advances. Scale backoff/growth happen
- *     here.
+ *   - "checked" (skip_on_overflow 1 or max_grad_norm > 0, not optimistic):
+ *     the caller has already run zero_grad_norm_overflow() on this step's
+ *     gradients with the same policy; if it set state->skipped, nothing but
+ *     the loss scale changes; otherwise the update is applied with g
+ *     multiplied by state->clip_coef, and the step advances. Scale
+ *     backoff/growth happen here.
+ *   - "optimistic" (skip_on_overflow 1, optimistic 1, no clipping): one pass
+ *     per group reads the current set (state->cur), writes the updated values
+ *     into the other set and into flat_param, and emits norm partials; then
+ *     without overflow the other set becomes current (cur flips) and the step
+ *     advances; with overflow the current set stays, the scale backs off, and
+ *     flat_param's slice is rewritten from the current master. That restores
+ *     it exactly when the slice held RNE16(current master) before the step,
+ *     as it does after zero_cast_writeback() or any applied step. Costs a
+ *     second state set (12 B/param) instead of the checked pipeline's extra
+ *     pass over an fp32 average.
  * `groups` is a host array; group g uses workspace slot g and the beta powers
  * state->beta*_pow[g].
  * Errors: INVALID_ARG, ALIGNMENT, WORKSPACE, UNSUPPORTED. */

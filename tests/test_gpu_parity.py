@@ -394,3 +394,49 @@ def test_checked_pipeline_with_clipping(n, n_d, dt, skip, max_norm, scale):
 
 def test_fused_pipeline_reports_no_clip():
     run_fused(5000, 2, "bf16", steps=2, seed=14)
+
+
+# --------------------------------------------------------------------------
+# optimistic pipeline: update into the second state set, commit or discard
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,n_d,dt,off,misalign", [(70_001, 8, "f16", 3, 0), (4099, 1, "bf16", 0, 0),
+                                                   (30_000, 2, "f16", 8, 1)])
+def test_optimistic_pipeline(n, n_d, dt, off, misalign):
+    tag = f"optimistic n={n} n_d={n_d} {dt} off={off} mis={misalign}"
+    print(f"[case] {tag}", flush=True)
+    odt = ORACLE_DT[dt]
+    pol = oracle.Policy(skip_on_overflow=True, growth_interval=2)
+    sc = zdp.policy(True, growth_interval=2, optimistic=True)
+    master0 = normal_f32_np(n, 0.02, (15, "master"))
+    flat0 = to16_bits_np(normal_f32_np(n + off + 2, 0.02, (15, "flat")), dt)
+    flat0[off:off + n] = to16_bits_np(master0, dt)   # the slice holds RNE16(master)
+
+    def fp32(x=None):
+        t = carve(n + 8, misalign, n, torch.float32)
+        return t.copy_(up32(x)) if x is not None else t.zero_()
+
+    grp = zdp.Group(fp32(master0), fp32(), fp32(), master_alt=fp32(), exp_avg_alt=fp32(), exp_avg_sq_alt=fp32(),
+                    flat_param=up16(flat0, dt), param_offset=off, weight_decay=0.1)
+    ws, st = zdp.new_workspace(1), zdp.new_state(65536.0)
+    og = oracle.Group(replicas=None, grad_dt=odt, master=master0.copy(), m=np.zeros(n, np.float32),
+                      v=np.zeros(n, np.float32), param=flat0[off:off + n].copy(), param_dt=odt, weight_decay=0.1)
+    ost = oracle.State(loss_scale=65536.0)
+    for k in range(7):
+        reps = [grads16_np(n, dt, ost.loss_scale, (15, "g", k, r)) for r in range(n_d)]
+        if k in (2, 3):
+            reps[-1] = reps[-1].copy()
+            reps[-1][(k * 7919) % n] = POS_INF[dt] if k == 2 else NEG_NAN[dt]
+        grp.replicas = [up16(r, dt) for r in reps]
+        zdp.adam_step([grp], ws, st, sc)
+        og.replicas = reps
+        oracle.step([og], pol, ost)
+        torch.cuda.synchronize()
+        s = _compare_state(f"{tag} call {k + 1}", st, ost)
+        cm, cmm, cv = zdp.current_state(grp, s)
+        _compare_group(f"{tag} call {k + 1}", cm, cmm, cv, og)
+        got = down16(grp.flat_param)
+        assert_u16_equal(got[off:off + n], og.param, f"{tag} call {k + 1} param")
+        outside = np.r_[0:off, off + n:flat0.size]
+        assert_u16_equal(got[outside], flat0[outside], f"{tag} param outside the slice")
+    assert ost.step == 5

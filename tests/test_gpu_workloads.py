@@ -78,9 +78,10 @@ class Run:
     """Device buffers of a workload (laid out as bench.py lays them out) and the
     oracle's copy of the sampled coordinates."""
 
-    def __init__(self, key, full=False):
+    def __init__(self, key, full=False, optimistic=False):
         self.wl = wl = WORKLOADS[key]
         self.full = full
+        self.optimistic = optimistic
         gdt, pdt = torch_dtype(wl.grad_dt), torch_dtype(wl.param_dt)
         self.odt = ORACLE_DT[wl.grad_dt]
         self.groups, self.ogroups, self.samples, self.outside = [], [], [], []
@@ -98,10 +99,14 @@ class Run:
             stride = ((n + 63) // 64) * 64
             gbuf = torch.empty(max(1, wl.n_d * stride), dtype=gdt, device=DEV)
             reps = [gbuf[r * stride:r * stride + n] for r in range(wl.n_d)]
+            alt = {}
+            if optimistic:
+                alt = dict(master_alt=torch.empty_like(master), exp_avg_alt=torch.empty_like(master),
+                           exp_avg_sq_alt=torch.empty_like(master))
             self.groups.append(zdp.Group(master=master, exp_avg=torch.zeros_like(master),
                                          exp_avg_sq=torch.zeros_like(master), replicas=reps,
                                          flat_param=flat, param_offset=off, lr=wl.lr, beta1=wl.beta1,
-                                         beta2=wl.beta2, eps=wl.eps, weight_decay=spec.weight_decay))
+                                         beta2=wl.beta2, eps=wl.eps, weight_decay=spec.weight_decay, **alt))
             # sample: tensor boundaries inside the shard, the middle (inf site)
             bounds = [sl[1] for sl in zdp.partition_tensors(list(spec.numels), wl.n_d, wl.rank)]
             idx = np.arange(n, dtype=np.int64) if full else _sample(n, bounds + [n // 2], gi + 17)
@@ -120,7 +125,7 @@ class Run:
         self.state = zdp.new_state(wl.loss_scale)
         self.ostate = oracle.State(loss_scale=wl.loss_scale)
         self.policy = oracle.Policy(skip_on_overflow=wl.dynamic_loss_scale)
-        self.policy_ = zdp.policy(True) if wl.dynamic_loss_scale else None
+        self.policy_ = zdp.policy(True, optimistic=optimistic) if wl.dynamic_loss_scale else None
         self.avg = [torch.empty_like(g.master) for g in self.groups] if wl.dynamic_loss_scale else None
 
     def draw_grads(self, call):
@@ -139,8 +144,8 @@ class Run:
         return False
 
     def gpu_step(self):
-        if self.policy_ is None:
-            zdp.adam_step(self.groups, self.ws, self.state)
+        if self.policy_ is None or self.optimistic:
+            zdp.adam_step(self.groups, self.ws, self.state, self.policy_)
             return
         for gi, g in enumerate(self.groups):
             zdp.reduce_grad_segment(g.replicas, self.avg[gi], self.ws, gi, self.state)
@@ -187,9 +192,10 @@ class Run:
                 assert abs(s["grad_norm_sq"] - self.ostate.norm2) <= 1e-10 * self.ostate.norm2, tag
             for g, og, idx in zip(self.groups, self.ogroups, self.samples):
                 tidx = torch.from_numpy(idx).to(DEV)
-                assert_bits_equal(down32(g.master[tidx]), og.master, tag + " master")
-                assert_bits_equal(down32(g.exp_avg[tidx]), og.m, tag + " exp_avg")
-                assert_bits_equal(down32(g.exp_avg_sq[tidx]), og.v, tag + " exp_avg_sq")
+                cm, cmm, cv = zdp.current_state(g, s)
+                assert_bits_equal(down32(cm[tidx]), og.master, tag + " master")
+                assert_bits_equal(down32(cmm[tidx]), og.m, tag + " exp_avg")
+                assert_bits_equal(down32(cv[tidx]), og.v, tag + " exp_avg_sq")
                 # the slice always holds the rounded master (initially too)
                 got = _u16(g.flat_param[tidx + g.param_offset])
                 want = oracle.encode16(og.master, ORACLE_DT[wl.param_dt])
@@ -233,9 +239,10 @@ def test_7_5b_nd64():
 
 
 @pytest.mark.timeout(900)
-def test_13b_nd8_overflow_skip():
-    print("[workload] 13b_nd8", flush=True)
-    st = Run("13b_nd8").run(full_scan_calls=(1,))
+@pytest.mark.parametrize("pipeline", ["checked", "optimistic"])
+def test_13b_nd8_overflow_skip(pipeline):
+    print(f"[workload] 13b_nd8 ({pipeline})", flush=True)
+    st = Run("13b_nd8", optimistic=pipeline == "optimistic").run(full_scan_calls=(1,))
     # ten calls, the fourth overflows: nine applied steps, scale halved once
     assert st.step == 9 and st.loss_scale == 32768.0
     _free()

@@ -55,11 +55,14 @@ class StepState(ctypes.Structure):
                 ("overflow", ctypes.c_int32),
                 ("skipped", ctypes.c_int32),
                 ("good_steps", ctypes.c_int32),
-                ("clip_coef", ctypes.c_float)]
+                ("clip_coef", ctypes.c_float),
+                ("cur", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class Policy(ctypes.Structure):
     _fields_ = [("skip_on_overflow", ctypes.c_int32), ("growth_interval", ctypes.c_int32),
+                ("optimistic", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("backoff", ctypes.c_double), ("growth", ctypes.c_double),
                 ("min_scale", ctypes.c_double), ("max_grad_norm", ctypes.c_double)]
 
@@ -73,6 +76,9 @@ class _Group(ctypes.Structure):
                 ("master", ctypes.c_void_p),
                 ("exp_avg", ctypes.c_void_p),
                 ("exp_avg_sq", ctypes.c_void_p),
+                ("master_alt", ctypes.c_void_p),
+                ("exp_avg_alt", ctypes.c_void_p),
+                ("exp_avg_sq_alt", ctypes.c_void_p),
                 ("flat_param", ctypes.c_void_p),
                 ("param_offset", ctypes.c_int64),
                 ("param_dt", ctypes.c_int32),
@@ -207,7 +213,7 @@ def read_state(state):
     return {"beta1_pow": list(s.beta1_pow), "beta2_pow": list(s.beta2_pow),
             "grad_norm_sq": s.grad_norm_sq, "grad_norm": s.grad_norm, "loss_scale": s.loss_scale,
             "step": s.step, "overflow": s.overflow, "skipped": s.skipped, "good_steps": s.good_steps,
-            "clip_coef": s.clip_coef}
+            "clip_coef": s.clip_coef, "cur": s.cur}
 
 
 def new_workspace(n_groups, device="cuda"):
@@ -220,15 +226,18 @@ def new_workspace(n_groups, device="cuda"):
 
 
 def policy(skip_on_overflow=False, growth_interval=1000, backoff=0.5, growth=2.0, min_scale=1.0,
-           max_grad_norm=0.0):
+           max_grad_norm=0.0, optimistic=False):
     """Loss-scale and clipping policy. Skipping or clipping selects the checked
-    pipeline: reduce_grad_segment / grad_norm_overflow before adam_step."""
-    return Policy(int(bool(skip_on_overflow)), int(growth_interval), float(backoff), float(growth),
-                  float(min_scale), float(max_grad_norm))
+    pipeline (reduce_grad_segment / grad_norm_overflow before adam_step), or,
+    with optimistic=True (skip, no clipping), the optimistic pipeline, which
+    needs each group's *_alt state set."""
+    return Policy(int(bool(skip_on_overflow)), int(growth_interval), int(bool(optimistic)), 0,
+                  float(backoff), float(growth), float(min_scale), float(max_grad_norm))
 
 
 def is_checked(policy_):
-    return policy_ is not None and (policy_.skip_on_overflow or policy_.max_grad_norm > 0)
+    return (policy_ is not None and not policy_.optimistic
+            and (policy_.skip_on_overflow or policy_.max_grad_norm > 0))
 
 
 def reduce_grad_segment(replicas, avg_out, workspace, group, state, stream=None):
@@ -270,6 +279,9 @@ class Group:
     exp_avg_sq: object
     replicas: list = None      # N_d 16-bit tensors (fused average)
     avg: object = None         # or an fp32 average from reduce_grad_segment
+    master_alt: object = None  # optimistic pipeline: second state set
+    exp_avg_alt: object = None
+    exp_avg_sq_alt: object = None
     flat_param: object = None  # 16-bit flat vector (whole group) or None
     param_offset: int = 0
     lr: float = 1e-3
@@ -301,6 +313,15 @@ def _group_struct(g, keep):
         if getattr(g, name).numel() != n:
             raise ValueError(f"{name} length differs from master")
     s.master, s.exp_avg, s.exp_avg_sq = g.master.data_ptr(), g.exp_avg.data_ptr(), g.exp_avg_sq.data_ptr()
+    if g.master_alt is not None:
+        for name in ("master_alt", "exp_avg_alt", "exp_avg_sq_alt"):
+            if getattr(g, name) is None or getattr(g, name).numel() != n:
+                raise ValueError(f"{name} missing or of the wrong length")
+        s.master_alt = g.master_alt.data_ptr()
+        s.exp_avg_alt = g.exp_avg_alt.data_ptr()
+        s.exp_avg_sq_alt = g.exp_avg_sq_alt.data_ptr()
+    else:
+        s.master_alt = s.exp_avg_alt = s.exp_avg_sq_alt = None
     if g.flat_param is not None:
         if g.param_offset + n > g.flat_param.numel():
             raise ValueError("param_offset + n exceeds the flat parameter vector")
@@ -321,6 +342,14 @@ def adam_step(groups, workspace, state, policy_=None, stream=None):
     sc = ctypes.byref(policy_) if policy_ is not None else None
     _check(load().zero_adam_step(arr, len(groups), sc, _ptr(workspace), _nbytes(workspace), _ptr(state),
                                  _stream(stream)))
+
+
+def current_state(group, state_dict):
+    """(master, exp_avg, exp_avg_sq) tensors holding the current state of a
+    group, given read_state()'s result (the optimistic pipeline alternates)."""
+    if state_dict.get("cur", 0) and group.master_alt is not None:
+        return group.master_alt, group.exp_avg_alt, group.exp_avg_sq_alt
+    return group.master, group.exp_avg, group.exp_avg_sq
 
 
 def cast_writeback(master, flat_param, offset, stream=None):

@@ -309,7 +309,11 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_policy
   if (int rc = check_workspace(workspace, workspace_bytes)) return rc;
   if (int rc = check_policy(policy)) return rc;
   const bool dynamic = policy && policy->skip_on_overflow;
-  const bool checked = policy && (policy->skip_on_overflow || policy->max_grad_norm > 0.0);
+  const bool optimistic = policy && policy->optimistic;
+  if (optimistic && (!dynamic || policy->max_grad_norm > 0.0))
+    return fail(ZERO_ERR_INVALID_ARG, "the optimistic pipeline needs skip_on_overflow and no clipping");
+  const bool checked = !optimistic && policy && (policy->skip_on_overflow || policy->max_grad_norm > 0.0);
+  const int mode = optimistic ? kOptimistic : (checked ? kChecked : kFused);
   AdamArgs A[ZERO_MAX_GROUPS];
   int src[ZERO_MAX_GROUPS];
   bool vec[ZERO_MAX_GROUPS];
@@ -323,6 +327,16 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_policy
     if (!aligned(G.master, 4) || !aligned(G.exp_avg, 4) || !aligned(G.exp_avg_sq, 4))
       return fail(ZERO_ERR_ALIGNMENT, "group %d: fp32 state not 4-byte aligned", g);
     bool v = aligned(G.master, 16) && aligned(G.exp_avg, 16) && aligned(G.exp_avg_sq, 16);
+    if (optimistic) {
+      if ((!G.master_alt || !G.exp_avg_alt || !G.exp_avg_sq_alt) && G.n > 0)
+        return fail(ZERO_ERR_INVALID_ARG, "group %d: the optimistic pipeline needs the *_alt state set", g);
+      if (!aligned(G.master_alt, 4) || !aligned(G.exp_avg_alt, 4) || !aligned(G.exp_avg_sq_alt, 4))
+        return fail(ZERO_ERR_ALIGNMENT, "group %d: fp32 *_alt state not 4-byte aligned", g);
+      v = v && aligned(G.master_alt, 16) && aligned(G.exp_avg_alt, 16) && aligned(G.exp_avg_sq_alt, 16);
+      a.master_alt = G.master_alt;
+      a.m_alt = G.exp_avg_alt;
+      a.v_alt = G.exp_avg_sq_alt;
+    }
     if ((G.replicas != nullptr) == (G.avg != nullptr) && !(G.n == 0 && !G.replicas))
       return fail(ZERO_ERR_INVALID_ARG, "group %d: give exactly one of replicas and avg", g);
     if (G.avg || !G.replicas) {
@@ -370,7 +384,7 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_policy
   if (int rc = check_device()) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   for (int32_t g = 0; g < n_groups; ++g) {
-    hipError_t e = launch_adam(A[g], src[g], vec[g], checked, s);
+    hipError_t e = launch_adam(A[g], src[g], vec[g], mode, s);
     if (e != hipSuccess) return hip_fail(e, "update launch");
     if (!checked) {
       e = fold_into(workspace, g, A[g].n, s);
@@ -383,13 +397,39 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_policy
     F.level2 = level2_of(workspace, 0);
     F.state = state;
     F.n_groups = n_groups;
-    F.mode = 1;
+    F.mode = optimistic ? 2 : 1;
+    if (optimistic) {
+      F.skip_on_overflow = 1;
+      F.growth_interval = policy->growth_interval;
+      F.backoff = policy->backoff;
+      F.growth = policy->growth;
+      F.min_scale = policy->min_scale;
+    }
     for (int32_t g = 0; g < n_groups; ++g) {
       F.beta1[g] = groups[g].beta1;
       F.beta2[g] = groups[g].beta2;
     }
     hipError_t e = launch_finalize(F, s);
-    return e == hipSuccess ? ZERO_OK : hip_fail(e, "finalize launch");
+    if (e != hipSuccess) return hip_fail(e, "finalize launch");
+    if (optimistic) {
+      // a voided step already wrote its values into the parameter slices:
+      // rewrite them from the current master (the launch exits at once otherwise)
+      for (int32_t g = 0; g < n_groups; ++g) {
+        if (!A[g].param || A[g].n == 0) continue;
+        RestoreArgs R;
+        R.master = A[g].master;
+        R.master_alt = A[g].master_alt;
+        R.n = A[g].n;
+        R.param = A[g].param;
+        R.param_dt = A[g].param_dt;
+        R.param_align = A[g].param_align;
+        R.state = state;
+        const bool rv = aligned(R.master, 16) && aligned(R.master_alt, 16);
+        e = launch_restore(R, rv, s);
+        if (e != hipSuccess) return hip_fail(e, "restore launch");
+      }
+    }
+    return ZERO_OK;
   }
   CommitArgs C;
   memset(&C, 0, sizeof C);

@@ -216,17 +216,35 @@ __device__ __forceinline__ void write_block_partial(double s, int bad, double* o
 
 // ------------------------------------------------------------------------
 // The update kernel
-//   CHECKED = false (fused): average, norm partials, Adam, writeback.
-//   CHECKED = true: exits if the step was voided; no partials.
+//   kFused: average, norm partials, Adam, writeback.
+//   kChecked: exits if the step was voided; clip multiplier; no partials.
+//   kOptimistic: as kFused, but reads the current state set and writes the
+//     other one (state->cur picks which is which).
 // VEC: fp32 arrays 16-byte and 16-bit copies 8-byte aligned (quad path).
 // ------------------------------------------------------------------------
 
-template <int SRC, bool VEC, bool CHECKED>
+template <int SRC, bool VEC, int MODE>
 __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs A) {
+  constexpr bool CHECKED = MODE == kChecked;
   if constexpr (CHECKED) {
     if (A.state->skipped) return;
   }
   const Scalars s = load_scalars(A);
+  const float* mst_in = A.master;
+  const float* m_in = A.m;
+  const float* v_in = A.v;
+  float* mst_out = A.master;
+  float* m_out = A.m;
+  float* v_out = A.v;
+  if constexpr (MODE == kOptimistic) {
+    const bool alt_is_current = A.state->cur != 0;
+    mst_in = alt_is_current ? A.master_alt : A.master;
+    m_in = alt_is_current ? A.m_alt : A.m;
+    v_in = alt_is_current ? A.v_alt : A.v;
+    mst_out = alt_is_current ? A.master : A.master_alt;
+    m_out = alt_is_current ? A.m : A.m_alt;
+    v_out = alt_is_current ? A.v : A.v_alt;
+  }
   double sumsq = 0.0;
   int bad = 0;
   const int pdt = A.param_dt;
@@ -239,11 +257,11 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs A) {
     float g = a * s.inv_scale;
     if constexpr (!CHECKED) account(a, g, sumsq, bad);
     if constexpr (CHECKED) g = g * s.clip;
-    float th = A.master[j], m = A.m[j], v = A.v[j];
+    float th = mst_in[j], m = m_in[j], v = v_in[j];
     adam1(g, th, m, v, s);
-    A.master[j] = th;
-    A.m[j] = m;
-    A.v[j] = v;
+    mst_out[j] = th;
+    m_out[j] = m;
+    v_out[j] = v;
     if (pdt) param[j] = static_cast<uint16_t>(encode16(th, pdt));
   };
 
@@ -254,9 +272,9 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs A) {
       if (VEC && e + 4 <= n) {
         float a[4];
         source4<SRC>(A.src, e, a);
-        const f4 t4 = *reinterpret_cast<const f4*>(A.master + e);
-        const f4 m4 = *reinterpret_cast<const f4*>(A.m + e);
-        const f4 v4 = *reinterpret_cast<const f4*>(A.v + e);
+        const f4 t4 = *reinterpret_cast<const f4*>(mst_in + e);
+        const f4 m4 = *reinterpret_cast<const f4*>(m_in + e);
+        const f4 v4 = *reinterpret_cast<const f4*>(v_in + e);
         float th[4] = {t4.x, t4.y, t4.z, t4.w};
         float mm[4] = {m4.x, m4.y, m4.z, m4.w};
         float vv[4] = {v4.x, v4.y, v4.z, v4.w};
@@ -267,9 +285,9 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs A) {
           if constexpr (CHECKED) g = g * s.clip;
           adam1(g, th[q], mm[q], vv[q], s);
         }
-        *reinterpret_cast<f4*>(A.master + e) = (f4){th[0], th[1], th[2], th[3]};
-        *reinterpret_cast<f4*>(A.m + e) = (f4){mm[0], mm[1], mm[2], mm[3]};
-        *reinterpret_cast<f4*>(A.v + e) = (f4){vv[0], vv[1], vv[2], vv[3]};
+        *reinterpret_cast<f4*>(mst_out + e) = (f4){th[0], th[1], th[2], th[3]};
+        *reinterpret_cast<f4*>(m_out + e) = (f4){mm[0], mm[1], mm[2], mm[3]};
+        *reinterpret_cast<f4*>(v_out + e) = (f4){vv[0], vv[1], vv[2], vv[3]};
         if (pdt) {
           uint32_t h[4];
 #pragma unroll
@@ -372,6 +390,29 @@ __global__ void __launch_bounds__(kBlock) finalize_kernel(const FinalizeArgs F) 
       st->beta1_pow[g] = st->beta1_pow[g] * F.beta1[g];
       st->beta2_pow[g] = st->beta2_pow[g] * F.beta2[g];
     }
+  } else if (F.mode == 2) {
+    // optimistic: the update went to the other state set; keep it or drop it
+    st->clip_coef = 1.0f;
+    if (flag) {
+      st->skipped = 1;
+      double sc = static_cast<double>(st->loss_scale) * F.backoff;
+      if (sc < F.min_scale) sc = F.min_scale;
+      st->loss_scale = static_cast<float>(sc);
+      st->good_steps = 0;
+    } else {
+      st->skipped = 0;
+      st->cur = st->cur ^ 1;
+      st->step = st->step + 1;
+      for (int g = 0; g < F.n_groups; ++g) {
+        st->beta1_pow[g] = st->beta1_pow[g] * F.beta1[g];
+        st->beta2_pow[g] = st->beta2_pow[g] * F.beta2[g];
+      }
+      st->good_steps = st->good_steps + 1;
+      if (F.growth_interval > 0 && st->good_steps == F.growth_interval) {
+        st->loss_scale = static_cast<float>(static_cast<double>(st->loss_scale) * F.growth);
+        st->good_steps = 0;
+      }
+    }
   } else {
     st->skipped = (flag && F.skip_on_overflow) ? 1 : 0;
     // clip multiplier min(1, max_norm / (norm + 1e-6)), fp64, rounded once
@@ -422,6 +463,8 @@ __global__ void state_init_kernel(zero_step_state* st, float loss_scale) {
   st->skipped = 0;
   st->good_steps = 0;
   st->clip_coef = 1.0f;
+  st->cur = 0;
+  st->reserved = 0;
 }
 
 // ------------------------------------------------------------------------
@@ -450,9 +493,39 @@ __global__ void __launch_bounds__(kBlock) cast_kernel(const CastArgs C) {
   }
 }
 
-template <int SRC, bool VEC, bool CHECKED>
+// Voided optimistic step: rewrite the parameter slice from the current master.
+// A small resident grid, so that the launch costs little when there is
+// nothing to do (the common case).
+constexpr int kRestoreGrid = 1024;
+
+template <bool VEC>
+__global__ void __launch_bounds__(kBlock) restore_kernel(const RestoreArgs R) {
+  const zero_step_state* st = R.state;
+  if (!st->skipped) return;
+  const float* master = st->cur ? R.master_alt : R.master;
+  uint16_t* const p16 = static_cast<uint16_t*>(R.param);
+  const int64_t n = R.n;
+  const int64_t ntiles = (n + kTile - 1) / kTile;
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+#pragma unroll
+    for (int k = 0; k < kQuadsPerThread; ++k) {
+      const int64_t e = t * kTile + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4;
+      if (VEC && e + 4 <= n) {
+        const f4 x = *reinterpret_cast<const f4*>(master + e);
+        const uint32_t h[4] = {encode16(x.x, R.param_dt), encode16(x.y, R.param_dt),
+                               encode16(x.z, R.param_dt), encode16(x.w, R.param_dt)};
+        store4_16(p16 + e, h, R.param_align);
+      } else {
+        for (int q = 0; q < 4; ++q)
+          if (e + q < n) p16[e + q] = static_cast<uint16_t>(encode16(master[e + q], R.param_dt));
+      }
+    }
+  }
+}
+
+template <int SRC, bool VEC, int MODE>
 hipError_t adam_launch(const AdamArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((adam_kernel<SRC, VEC, CHECKED>), dim3(stream_grid(a.n)), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL((adam_kernel<SRC, VEC, MODE>), dim3(stream_grid(a.n)), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
@@ -464,19 +537,35 @@ hipError_t reduce_launch(const ReduceArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_adam(const AdamArgs& a, int src, bool vec, bool checked, hipStream_t s) {
+hipError_t launch_adam(const AdamArgs& a, int src, bool vec, int mode, hipStream_t s) {
+#define ZDP_ADAM_MODE(SRC, VEC)                                               \
+  switch (mode) {                                                             \
+    case kFused: return adam_launch<SRC, VEC, kFused>(a, s);                  \
+    case kChecked: return adam_launch<SRC, VEC, kChecked>(a, s);              \
+    case kOptimistic: return adam_launch<SRC, VEC, kOptimistic>(a, s);        \
+    default: return hipErrorInvalidValue;                                     \
+  }
 #define ZDP_ADAM(SRC)                                                         \
   if (src == SRC) {                                                           \
-    if (vec) return checked ? adam_launch<SRC, true, true>(a, s)              \
-                            : adam_launch<SRC, true, false>(a, s);            \
-    return checked ? adam_launch<SRC, false, true>(a, s)                      \
-                   : adam_launch<SRC, false, false>(a, s);                    \
+    if (vec) { ZDP_ADAM_MODE(SRC, true) }                                     \
+    ZDP_ADAM_MODE(SRC, false)                                                 \
   }
   ZDP_ADAM(kSrcAvg)
   ZDP_ADAM(kSrcF16)
   ZDP_ADAM(kSrcBF16)
 #undef ZDP_ADAM
+#undef ZDP_ADAM_MODE
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_restore(const RestoreArgs& a, bool vec, hipStream_t s) {
+  int grid = stream_grid(a.n);
+  if (grid > kRestoreGrid) grid = kRestoreGrid;
+  if (vec)
+    hipLaunchKernelGGL(restore_kernel<true>, dim3(grid), dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL(restore_kernel<false>, dim3(grid), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_reduce(const ReduceArgs& a, int src, bool vec, hipStream_t s) {

@@ -45,6 +45,9 @@ struct AdamArgs {
   float* master;
   float* m;
   float* v;
+  float* master_alt;    // optimistic pipeline: the second state set
+  float* m_alt;
+  float* v_alt;
   void* param;          // flat_param + param_offset (already offset), or null
   int32_t param_dt;     // ZERO_DT_F16 / ZERO_DT_BF16 / 0
   int32_t param_align;  // 8, 4 or 2: largest power-of-two alignment of param, capped at 8
@@ -53,7 +56,7 @@ struct AdamArgs {
   int32_t has_decay;
   int32_t group;
   const zero_step_state* state;
-  double* partials;  // one per block (fused pipeline); null in the checked pipeline
+  double* partials;  // one per block (fused and optimistic pipelines); null in the checked one
 };
 
 // Arguments of the average kernel (checked pipeline) and of the single-copy scan.
@@ -77,10 +80,12 @@ struct FinalizeArgs {
   const double* level2;  // ZERO_MAX_GROUPS x kFoldBlocks
   zero_step_state* state;
   int32_t n_groups;
-  int32_t mode;  // 0: norm, skip verdict, clip multiplier; 1: norm, then commit a static-scale step
+  int32_t mode;  // 0: norm, skip verdict, clip multiplier; 1: norm, then commit a static-scale step;
+                 // 2: norm, then commit or discard an optimistic step (dynamic scale)
   int32_t skip_on_overflow;
-  int32_t pad;
-  double max_grad_norm;  // mode 0: clip threshold (0 = none)
+  int32_t growth_interval;  // mode 2
+  double max_grad_norm;     // mode 0: clip threshold (0 = none)
+  double backoff, growth, min_scale;  // mode 2
   double beta1[ZERO_MAX_GROUPS];
   double beta2[ZERO_MAX_GROUPS];
 };
@@ -104,7 +109,19 @@ struct CastArgs {
   int32_t param_align;
 };
 
+// Rewrite a group's parameter slice from its current master when the step was voided.
+struct RestoreArgs {
+  const float* master;
+  const float* master_alt;
+  int64_t n;
+  void* param;  // already offset
+  int32_t param_dt;
+  int32_t param_align;
+  const zero_step_state* state;
+};
+
 enum SrcKind { kSrcAvg = 0, kSrcF16 = 1, kSrcBF16 = 2 };
+enum StepMode { kFused = 0, kChecked = 1, kOptimistic = 2 };
 
 // Blocks of a streaming launch over n elements.
 inline int stream_grid(int64_t n) {
@@ -115,12 +132,13 @@ inline int stream_grid(int64_t n) {
 
 // Launchers (kernels.hip). Each returns the hipError_t of its launches.
 // `vec` selects the aligned quad path.
-hipError_t launch_adam(const AdamArgs& a, int src_kind, bool vec, bool checked, hipStream_t s);
+hipError_t launch_adam(const AdamArgs& a, int src_kind, bool vec, int mode, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, int src_kind, bool vec, hipStream_t s);
 hipError_t launch_fold(const FoldArgs& a, hipStream_t s);
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
 hipError_t launch_commit(const CommitArgs& a, hipStream_t s);
 hipError_t launch_state_init(zero_step_state* st, float loss_scale, hipStream_t s);
 hipError_t launch_cast(const CastArgs& a, bool vec, hipStream_t s);
+hipError_t launch_restore(const RestoreArgs& a, bool vec, hipStream_t s);
 
 }  // namespace zdp
