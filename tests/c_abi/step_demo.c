@@ -1,0 +1,180 @@
+/*
+ * A plain C consumer of the zero_dp C ABI: no torch, no Python.
+ *
+ * Lays out one rank's shard the way a training loop would (rank `rank` of
+ * `n_d` over a flat fp16 vector of `psi` elements), fills the inputs from a
+ * fixed integer recipe, runs `steps` fused steps on the null stream, and
+ * writes the inputs and results to a binary file for the test to check
+ * against the CPU oracle:
+ *
+ *   step_demo OUT PSI N_D RANK STEPS
+ *
+ * File layout (little endian): int64 psi, n_d, rank, offset, size, steps;
+ * uint16 replicas[steps][n_d][size]; float master0[size];
+ * float master[size], m[size], v[size]; uint16 flat[psi] (after);
+ * uint16 flat0[psi] (before); double grad_norm_sq; int64 step.
+ */
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "zero_dp.h"
+
+#define HIP_OK(x)                                                             \
+  do {                                                                        \
+    hipError_t e_ = (x);                                                      \
+    if (e_ != hipSuccess) {                                                   \
+      fprintf(stderr, "HIP error %s at line %d\n", hipGetErrorString(e_), __LINE__); \
+      exit(2);                                                                \
+    }                                                                         \
+  } while (0)
+
+#define ZERO_OK_OR_DIE(x)                                                     \
+  do {                                                                        \
+    int rc_ = (x);                                                            \
+    if (rc_ != ZERO_OK) {                                                     \
+      fprintf(stderr, "zero_dp error %d: %s (line %d)\n", rc_, zero_last_error(), __LINE__); \
+      exit(3);                                                                \
+    }                                                                         \
+  } while (0)
+
+/* a small deterministic integer mix, turned into fp16 bits of a modest value */
+static uint32_t mix(uint64_t x) {
+  x ^= x >> 33;
+  x *= 0xff51afd7ed558ccdULL;
+  x ^= x >> 33;
+  x *= 0xc4ceb9fe1a85ec53ULL;
+  x ^= x >> 33;
+  return (uint32_t)x;
+}
+
+static uint16_t grad_bits(uint64_t key) {
+  /* fp16 with exponent 5..14 (values about 3e-5 .. 0.5), random sign and mantissa */
+  uint32_t h = mix(key);
+  uint16_t sign = (uint16_t)((h >> 31) << 15);
+  uint16_t expo = (uint16_t)(5 + (h >> 10) % 10);
+  uint16_t frac = (uint16_t)(h & 0x3ff);
+  return sign | (uint16_t)(expo << 10) | frac;
+}
+
+int main(int argc, char** argv) {
+  if (argc != 6) {
+    fprintf(stderr, "usage: %s OUT PSI N_D RANK STEPS\n", argv[0]);
+    return 1;
+  }
+  const char* out_path = argv[1];
+  const int64_t psi = atoll(argv[2]);
+  const int32_t n_d = atoi(argv[3]);
+  const int32_t rank = atoi(argv[4]);
+  const int64_t steps = atoll(argv[5]);
+  if (n_d < 1 || n_d > 64 || rank < 0 || rank >= n_d || psi < 1 || steps < 1) {
+    fprintf(stderr, "bad arguments\n");
+    return 1;
+  }
+
+  zero_segment* segs = malloc(sizeof(zero_segment) * (size_t)n_d);
+  ZERO_OK_OR_DIE(zero_partition(psi, n_d, 1, segs, NULL));
+  const int64_t off = segs[rank].offset, n = segs[rank].size;
+  free(segs);
+
+  /* host inputs */
+  uint16_t* flat0 = malloc(sizeof(uint16_t) * (size_t)psi);
+  for (int64_t i = 0; i < psi; ++i) flat0[i] = grad_bits(0x5eed0000ULL + (uint64_t)i);
+  float* master0 = malloc(sizeof(float) * (size_t)n);
+  for (int64_t j = 0; j < n; ++j) master0[j] = ((float)(mix(0xabcULL + (uint64_t)j) % 20001) - 10000.0f) * 2e-6f;
+  uint16_t* reps = malloc(sizeof(uint16_t) * (size_t)(steps * n_d * n));
+  for (int64_t k = 0; k < steps; ++k)
+    for (int32_t r = 0; r < n_d; ++r)
+      for (int64_t j = 0; j < n; ++j)
+        reps[(k * n_d + r) * n + j] = grad_bits(((uint64_t)k << 48) ^ ((uint64_t)r << 40) ^ (uint64_t)(off + j));
+
+  /* device buffers, owned here */
+  float *d_master, *d_m, *d_v;
+  uint16_t *d_flat, *d_reps;
+  void *d_ws, *d_state;
+  const size_t ws_bytes = zero_workspace_bytes(1);
+  HIP_OK(hipMalloc((void**)&d_master, sizeof(float) * (size_t)n));
+  HIP_OK(hipMalloc((void**)&d_m, sizeof(float) * (size_t)n));
+  HIP_OK(hipMalloc((void**)&d_v, sizeof(float) * (size_t)n));
+  HIP_OK(hipMalloc((void**)&d_flat, sizeof(uint16_t) * (size_t)psi));
+  HIP_OK(hipMalloc((void**)&d_reps, sizeof(uint16_t) * (size_t)(n_d * n)));
+  HIP_OK(hipMalloc(&d_ws, ws_bytes));
+  HIP_OK(hipMalloc(&d_state, sizeof(zero_step_state)));
+  HIP_OK(hipMemcpy(d_master, master0, sizeof(float) * (size_t)n, hipMemcpyHostToDevice));
+  HIP_OK(hipMemset(d_m, 0, sizeof(float) * (size_t)n));
+  HIP_OK(hipMemset(d_v, 0, sizeof(float) * (size_t)n));
+  HIP_OK(hipMemcpy(d_flat, flat0, sizeof(uint16_t) * (size_t)psi, hipMemcpyHostToDevice));
+  ZERO_OK_OR_DIE(zero_state_init((zero_step_state*)d_state, 1.0f, NULL));
+
+  const void* rep_ptrs[64];
+  for (int32_t r = 0; r < n_d; ++r) rep_ptrs[r] = d_reps + (size_t)r * (size_t)n;
+  zero_group g;
+  memset(&g, 0, sizeof g);
+  g.n = n;
+  g.replicas = rep_ptrs;
+  g.n_d = n_d;
+  g.grad_dt = ZERO_DT_F16;
+  g.master = d_master;
+  g.exp_avg = d_m;
+  g.exp_avg_sq = d_v;
+  g.flat_param = d_flat;
+  g.param_offset = off;
+  g.param_dt = ZERO_DT_F16;
+  g.lr = 1e-3;
+  g.beta1 = 0.9;
+  g.beta2 = 0.999;
+  g.eps = 1e-8;
+  g.weight_decay = 0.01;
+  for (int64_t k = 0; k < steps; ++k) {
+    HIP_OK(hipMemcpy(d_reps, reps + k * n_d * n, sizeof(uint16_t) * (size_t)(n_d * n), hipMemcpyHostToDevice));
+    ZERO_OK_OR_DIE(zero_adam_step(&g, 1, NULL, d_ws, ws_bytes, (zero_step_state*)d_state, NULL));
+  }
+  HIP_OK(hipDeviceSynchronize());
+
+  float* master = malloc(sizeof(float) * (size_t)n);
+  float* m = malloc(sizeof(float) * (size_t)n);
+  float* v = malloc(sizeof(float) * (size_t)n);
+  uint16_t* flat = malloc(sizeof(uint16_t) * (size_t)psi);
+  zero_step_state st;
+  HIP_OK(hipMemcpy(master, d_master, sizeof(float) * (size_t)n, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(m, d_m, sizeof(float) * (size_t)n, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(v, d_v, sizeof(float) * (size_t)n, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(flat, d_flat, sizeof(uint16_t) * (size_t)psi, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(&st, d_state, sizeof st, hipMemcpyDeviceToHost));
+
+  FILE* f = fopen(out_path, "wb");
+  if (!f) return 4;
+  const int64_t hdr[6] = {psi, n_d, rank, off, n, steps};
+  fwrite(hdr, sizeof hdr, 1, f);
+  fwrite(reps, sizeof(uint16_t), (size_t)(steps * n_d * n), f);
+  fwrite(master0, sizeof(float), (size_t)n, f);
+  fwrite(master, sizeof(float), (size_t)n, f);
+  fwrite(m, sizeof(float), (size_t)n, f);
+  fwrite(v, sizeof(float), (size_t)n, f);
+  fwrite(flat, sizeof(uint16_t), (size_t)psi, f);
+  fwrite(flat0, sizeof(uint16_t), (size_t)psi, f);
+  fwrite(&st.grad_norm_sq, sizeof(double), 1, f);
+  fwrite(&st.step, sizeof(int64_t), 1, f);
+  fclose(f);
+  printf("step_demo: psi=%lld n_d=%d rank=%d offset=%lld n=%lld steps=%lld norm=%g\n", (long long)psi, n_d,
+         rank, (long long)off, (long long)n, (long long)steps, (double)st.grad_norm);
+
+  hipFree(d_master);
+  hipFree(d_m);
+  hipFree(d_v);
+  hipFree(d_flat);
+  hipFree(d_reps);
+  hipFree(d_ws);
+  hipFree(d_state);
+  free(flat0);
+  free(master0);
+  free(reps);
+  free(master);
+  free(m);
+  free(v);
+  free(flat);
+  return 0;
+}

@@ -440,3 +440,72 @@ def test_optimistic_pipeline(n, n_d, dt, off, misalign):
         outside = np.r_[0:off, off + n:flat0.size]
         assert_u16_equal(got[outside], flat0[outside], f"{tag} param outside the slice")
     assert ost.step == 5
+
+
+# --------------------------------------------------------------------------
+# limits and concurrency
+# --------------------------------------------------------------------------
+
+def test_fused_at_the_replica_limit():
+    # N_d = ZERO_MAX_REPLICAS = 4096 copies in one strided buffer, ragged n
+    run_fused(1031, 4096, "bf16", steps=2, layout="strided", seed=21)
+
+
+def test_reduce_at_the_replica_limit_and_beyond():
+    n, n_d, dt = 3001, 4096, "f16"
+    reps = [grads16_np(n, dt, 1.0, (22, r)) for r in range(n_d)]
+    avg = torch.empty(n, dtype=torch.float32, device=DEV)
+    ws, st = zdp.new_workspace(1), zdp.new_state(1.0)
+    dreps = _replicas_on_device(reps, dt, "strided")
+    zdp.reduce_grad_segment(dreps, avg, ws, 0, st)
+    zdp.grad_norm_overflow(None, ws, 1, st)
+    want = oracle.average(reps, ORACLE_DT[dt])
+    assert_bits_equal(down32(avg), want, "average of 4096 copies")
+    n2, _ = oracle.norm_overflow(want, 1.0)
+    assert abs(zdp.read_state(st)["grad_norm_sq"] - n2) <= NORM_RTOL * n2
+    # one more copy than the limit is refused before any launch
+    stride = dreps[1].data_ptr() - dreps[0].data_ptr()
+    buf = torch.zeros((n_d + 1) * (stride // 2), dtype=torch.float16, device=DEV)
+    over = [buf[r * (stride // 2):r * (stride // 2) + n] for r in range(n_d + 1)]
+    with pytest.raises(zdp.ZeroError) as e:
+        zdp.reduce_grad_segment(over, avg, ws, 0, st)
+    assert e.value.code == zdp.ERR_UNSUPPORTED
+
+
+def test_two_streams_at_once():
+    # two independent shards (each with its own workspace and state) stepped
+    # concurrently on two streams; each must match its own oracle run
+    specs = [(300_007, 4, "f16", 3), (123_457, 2, "bf16", 0)]
+    steps = 3
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    sides = []
+    for i, (n, n_d, dt, off) in enumerate(specs):
+        odt = ORACLE_DT[dt]
+        master0 = normal_f32_np(n, 0.02, (23, i, "master"))
+        flat0 = to16_bits_np(normal_f32_np(off + n + 3, 0.02, (23, i, "flat")), dt)
+        reps = [[grads16_np(n, dt, 1.0, (23, i, k, r)) for r in range(n_d)] for k in range(steps)]
+        dev = dict(master=up32(master0), m=torch.zeros(n, device=DEV), v=torch.zeros(n, device=DEV),
+                   flat=up16(flat0, dt), reps=[[up16(b, dt) for b in rk] for rk in reps],
+                   ws=zdp.new_workspace(1), st=zdp.new_state(1.0))
+        og = oracle.Group(replicas=None, grad_dt=odt, master=master0.copy(), m=np.zeros(n, np.float32),
+                          v=np.zeros(n, np.float32), param=flat0[off:off + n].copy(), param_dt=odt,
+                          weight_decay=0.01)
+        ost = oracle.State()
+        for k in range(steps):
+            og.replicas = reps[k]
+            oracle.step([og], oracle.Policy(), ost)
+        sides.append((n, off, flat0, dev, og, ost))
+    torch.cuda.synchronize()
+    for k in range(steps):
+        for (n, off, _, dev, _, _), s in zip(sides, streams):
+            zdp.adam_step([zdp.Group(dev["master"], dev["m"], dev["v"], replicas=dev["reps"][k],
+                                     flat_param=dev["flat"], param_offset=off, weight_decay=0.01)],
+                          dev["ws"], dev["st"], stream=s)
+    torch.cuda.synchronize()
+    for i, (n, off, flat0, dev, og, ost) in enumerate(sides):
+        tag = f"stream {i}"
+        _compare_group(tag, dev["master"], dev["m"], dev["v"], og)
+        _compare_state(tag, dev["st"], ost)
+        got = down16(dev["flat"])
+        assert_u16_equal(got[off:off + n], og.param, f"{tag} param")
+        assert_u16_equal(np.delete(got, np.s_[off:off + n]), np.delete(flat0, np.s_[off:off + n]), f"{tag} outside")
