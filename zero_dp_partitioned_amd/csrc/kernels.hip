@@ -34,6 +34,23 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef unsigned u2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------------
+// Streaming accesses. Every byte a step touches is read once and written
+// once, so the vector loads and stores of the quad paths carry the
+// non-temporal hint: on gfx950 the read-modify-write of the fp32 state then
+// sustains a few per cent more HBM bandwidth than with the default policy.
+// ------------------------------------------------------------------------
+
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T* p) {
+  return __builtin_nontemporal_load(p);
+}
+
+template <typename T>
+__device__ __forceinline__ void st_stream(T* p, T x) {
+  __builtin_nontemporal_store(x, p);
+}
+
+// ------------------------------------------------------------------------
 // 16-bit encodings
 // ------------------------------------------------------------------------
 
@@ -66,10 +83,10 @@ __device__ __forceinline__ void store4_16(uint16_t* p, const uint32_t h[4], int 
     u2 w;
     w.x = w0;
     w.y = w1;
-    *reinterpret_cast<u2*>(p) = w;
+    st_stream(reinterpret_cast<u2*>(p), w);
   } else if (al == 4) {
-    reinterpret_cast<uint32_t*>(p)[0] = w0;
-    reinterpret_cast<uint32_t*>(p)[1] = w1;
+    st_stream(reinterpret_cast<uint32_t*>(p), w0);
+    st_stream(reinterpret_cast<uint32_t*>(p) + 1, w1);
   } else {
 #pragma unroll
     for (int k = 0; k < 4; ++k) p[k] = static_cast<uint16_t>(h[k]);
@@ -104,7 +121,7 @@ __device__ __forceinline__ float finish_average(float acc, const GradSource& S) 
 template <int SRC>
 __device__ __forceinline__ void source4(const GradSource& S, int64_t e, float a[4]) {
   if constexpr (SRC == kSrcAvg) {
-    const f4 x = *reinterpret_cast<const f4*>(S.avg + e);
+    const f4 x = ld_stream(reinterpret_cast<const f4*>(S.avg + e));
     a[0] = x.x;
     a[1] = x.y;
     a[2] = x.z;
@@ -117,11 +134,11 @@ __device__ __forceinline__ void source4(const GradSource& S, int64_t e, float a[
     for (; r + 8 <= nd; r += 8) {
       u2 x[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) x[q] = *reinterpret_cast<const u2*>(replica(S, r + q) + e);
+      for (int q = 0; q < 8; ++q) x[q] = ld_stream(reinterpret_cast<const u2*>(replica(S, r + q) + e));
 #pragma unroll
       for (int q = 0; q < 8; ++q) accumulate4<SRC>(acc, x[q]);
     }
-    for (; r < nd; ++r) accumulate4<SRC>(acc, *reinterpret_cast<const u2*>(replica(S, r) + e));
+    for (; r < nd; ++r) accumulate4<SRC>(acc, ld_stream(reinterpret_cast<const u2*>(replica(S, r) + e)));
 #pragma unroll
     for (int k = 0; k < 4; ++k) a[k] = finish_average(acc[k], S);
   }
@@ -272,9 +289,9 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs A) {
       if (VEC && e + 4 <= n) {
         float a[4];
         source4<SRC>(A.src, e, a);
-        const f4 t4 = *reinterpret_cast<const f4*>(mst_in + e);
-        const f4 m4 = *reinterpret_cast<const f4*>(m_in + e);
-        const f4 v4 = *reinterpret_cast<const f4*>(v_in + e);
+        const f4 t4 = ld_stream(reinterpret_cast<const f4*>(mst_in + e));
+        const f4 m4 = ld_stream(reinterpret_cast<const f4*>(m_in + e));
+        const f4 v4 = ld_stream(reinterpret_cast<const f4*>(v_in + e));
         float th[4] = {t4.x, t4.y, t4.z, t4.w};
         float mm[4] = {m4.x, m4.y, m4.z, m4.w};
         float vv[4] = {v4.x, v4.y, v4.z, v4.w};
@@ -285,9 +302,9 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs A) {
           if constexpr (CHECKED) g = g * s.clip;
           adam1(g, th[q], mm[q], vv[q], s);
         }
-        *reinterpret_cast<f4*>(mst_out + e) = (f4){th[0], th[1], th[2], th[3]};
-        *reinterpret_cast<f4*>(m_out + e) = (f4){mm[0], mm[1], mm[2], mm[3]};
-        *reinterpret_cast<f4*>(v_out + e) = (f4){vv[0], vv[1], vv[2], vv[3]};
+        st_stream(reinterpret_cast<f4*>(mst_out + e), (f4){th[0], th[1], th[2], th[3]});
+        st_stream(reinterpret_cast<f4*>(m_out + e), (f4){mm[0], mm[1], mm[2], mm[3]});
+        st_stream(reinterpret_cast<f4*>(v_out + e), (f4){vv[0], vv[1], vv[2], vv[3]});
         if (pdt) {
           uint32_t h[4];
 #pragma unroll
@@ -325,7 +342,7 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(const ReduceArgs R) {
         source4<SRC>(R.src, e, a);
 #pragma unroll
         for (int q = 0; q < 4; ++q) account(a[q], a[q] * inv_scale, sumsq, bad);
-        if (out) *reinterpret_cast<f4*>(out + e) = (f4){a[0], a[1], a[2], a[3]};
+        if (out) st_stream(reinterpret_cast<f4*>(out + e), (f4){a[0], a[1], a[2], a[3]});
       } else {
         for (int q = 0; q < 4; ++q) {
           if (e + q >= n) break;
@@ -481,7 +498,7 @@ __global__ void __launch_bounds__(kBlock) cast_kernel(const CastArgs C) {
     for (int k = 0; k < kQuadsPerThread; ++k) {
       const int64_t e = t * kTile + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4;
       if (VEC && e + 4 <= n) {
-        const f4 x = *reinterpret_cast<const f4*>(C.master + e);
+        const f4 x = ld_stream(reinterpret_cast<const f4*>(C.master + e));
         const uint32_t h[4] = {encode16(x.x, C.param_dt), encode16(x.y, C.param_dt),
                                encode16(x.z, C.param_dt), encode16(x.w, C.param_dt)};
         store4_16(p16 + e, h, C.param_align);
@@ -511,7 +528,7 @@ __global__ void __launch_bounds__(kBlock) restore_kernel(const RestoreArgs R) {
     for (int k = 0; k < kQuadsPerThread; ++k) {
       const int64_t e = t * kTile + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4;
       if (VEC && e + 4 <= n) {
-        const f4 x = *reinterpret_cast<const f4*>(master + e);
+        const f4 x = ld_stream(reinterpret_cast<const f4*>(master + e));
         const uint32_t h[4] = {encode16(x.x, R.param_dt), encode16(x.y, R.param_dt),
                                encode16(x.z, R.param_dt), encode16(x.w, R.param_dt)};
         store4_16(p16 + e, h, R.param_align);
