@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--pipeline", choices=["checked", "optimistic"], default="checked",
                    help="dynamic-loss-scale workloads: verdict before the update (checked) or an "
                         "update into a second state set committed afterwards (optimistic)")
+    p.add_argument("--placement", choices=["regions", "packed"], default="regions",
+                   help="buffers carved from one arena spread over HBM's 96 GiB regions (regions), or "
+                        "one allocation each in order (packed)")
     p.add_argument("--quiet", action="store_true")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="only run a plain device copy of BYTES bytes --steps times (to calibrate "
@@ -74,48 +77,55 @@ def log(args, *a):
 
 
 class Setup:
-    """Device buffers of one workload: per group the fp32 master / m / v shard,
-    the N_d 16-bit gradient copies of the shard (one buffer, 64-element padded
-    stride), and the group's whole 16-bit flat parameter vector."""
+    """Device buffers of one workload. Per group: fp32 master (seeded), m and v
+    (zero), the N_d 16-bit gradient copies of the shard, and the group's whole
+    16-bit flat parameter vector (plus a second state set for the optimistic
+    pipeline, or an fp32 average for the checked one), placed by
+    zero_dp_partitioned_amd.layout: "regions" (one arena spread over HBM's
+    96 GiB regions, the default) or "packed" (one allocation per buffer)."""
 
-    def __init__(self, wl, dev, optimistic=False):
-        import torch
+    def __init__(self, wl, dev, optimistic=False, placement="regions"):
         import zero_dp_partitioned_amd as zdp
+        from zero_dp_partitioned_amd import layout
         from workloads import derive_seed, fill_normal_, torch_dtype
 
         self.wl = wl
         self.groups = []
         self.shard = 0
-        gdt, pdt = torch_dtype(wl.grad_dt), torch_dtype(wl.param_dt)
-        for gi, spec in enumerate(wl.groups):
+        self.optimistic = optimistic and wl.dynamic_loss_scale
+        pipeline = ("optimistic" if self.optimistic else "checked") if wl.dynamic_loss_scale else "fused"
+        shards = []
+        for spec in wl.groups:
             psi = sum(spec.numels)
             segs, _ = zdp.partition(psi, wl.n_d)
-            off, n = segs[wl.rank]
-            master = torch.empty(n, dtype=torch.float32, device=dev)
+            shards.append((psi, *segs[wl.rank]))
+        table = placement == "regions" and wl.n_d <= layout.INLINE_COPIES
+        specs = layout.step_specs(shards, wl.n_d, torch_dtype(wl.grad_dt), torch_dtype(wl.param_dt),
+                                  pipeline, table)
+        buf, self.placement = layout.allocate(specs, dev, placement)
+        for gi, (spec, (psi, off, n)) in enumerate(zip(wl.groups, shards)):
+            master = buf[(gi, "master")][:n]
             fill_normal_(master, 0.02, derive_seed(wl.key, gi, "master"))
-            flat = torch.empty(psi, dtype=pdt, device=dev)
+            flat = buf[(gi, "flat")][:psi]
             fill_normal_(flat, 0.02, derive_seed(wl.key, gi, "flat"))
             flat[off:off + n].copy_(master)
-            stride = ((n + 63) // 64) * 64
-            gbuf = torch.empty(max(1, wl.n_d * stride), dtype=gdt, device=dev)
-            reps = [gbuf[r * stride:r * stride + n] for r in range(wl.n_d)]
+            reps = layout.copies_of(buf, gi, wl.n_d, n)
             for r, t in enumerate(reps):
                 fill_normal_(t, 1e-3, derive_seed(wl.key, gi, "grad", 0, r), scale=wl.loss_scale)
             alt = {}
-            if optimistic and wl.dynamic_loss_scale:
-                alt = dict(master_alt=torch.empty_like(master), exp_avg_alt=torch.empty_like(master),
-                           exp_avg_sq_alt=torch.empty_like(master))
+            if self.optimistic:
+                alt = {name: buf[(gi, name)][:n] for name in ("master_alt", "exp_avg_alt", "exp_avg_sq_alt")}
+            m, v = buf[(gi, "exp_avg")][:n].zero_(), buf[(gi, "exp_avg_sq")][:n].zero_()
             self.groups.append(zdp.Group(
-                master=master, exp_avg=torch.zeros_like(master), exp_avg_sq=torch.zeros_like(master),
+                master=master, exp_avg=m, exp_avg_sq=v,
                 replicas=reps, flat_param=flat, param_offset=off, lr=wl.lr, beta1=wl.beta1,
                 beta2=wl.beta2, eps=wl.eps, weight_decay=spec.weight_decay, **alt))
             self.shard += n
         self.ws = zdp.new_workspace(len(self.groups))
         self.state = zdp.new_state(wl.loss_scale)
-        self.optimistic = optimistic and wl.dynamic_loss_scale
         self.policy = zdp.policy(True, optimistic=self.optimistic) if wl.dynamic_loss_scale else None
-        if wl.dynamic_loss_scale and not self.optimistic:
-            self.avg = [torch.empty_like(g.master) for g in self.groups]
+        if pipeline == "checked":
+            self.avg = [buf[(gi, "avg")][:g.master.numel()] for gi, g in enumerate(self.groups)]
 
     def step(self):
         import zero_dp_partitioned_amd as zdp
@@ -186,7 +196,7 @@ def main():
     torch.cuda.set_device(dev)
     wl = WORKLOADS[args.workload]
     log(args, f"workload {wl.key}: {wl.title}")
-    setup = Setup(wl, dev, optimistic=args.pipeline == "optimistic")
+    setup = Setup(wl, dev, optimistic=args.pipeline == "optimistic", placement=args.placement)
     S = setup.shard
     bpp = bytes_per_param(wl.n_d)
     log(args, f"shard {S} params, {len(setup.groups)} group(s), {bpp} B/param, "
@@ -241,7 +251,7 @@ def main():
                    "loss_scale": wl.loss_scale, "dynamic_loss_scale": wl.dynamic_loss_scale,
                    "pipeline": ("optimistic" if setup.optimistic else "checked") if wl.dynamic_loss_scale
                    else "fused",
-                   "bytes_per_param": bpp},
+                   "bytes_per_param": bpp, **setup.placement},
         "gbps": achieved,
         "pct_peak": 100.0 * achieved / PEAK_HBM_GBPS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",

@@ -509,3 +509,37 @@ def test_two_streams_at_once():
         got = down16(dev["flat"])
         assert_u16_equal(got[off:off + n], og.param, f"{tag} param")
         assert_u16_equal(np.delete(got, np.s_[off:off + n]), np.delete(flat0, np.s_[off:off + n]), f"{tag} outside")
+
+
+def test_fused_step_in_a_planned_arena():
+    # every buffer carved from one arena at the offsets zero_plan_arena gives
+    # (64 MiB regions so that the arena stays small), three steps vs the oracle
+    n, n_d, dt, steps = 300_007, 3, "bf16", 3
+    odt = ORACLE_DT[dt]
+    sizes = [4 * n] * 3 + [2 * n] * n_d + [2 * n]
+    traffic = [8 * n] * 3 + [2 * n] * n_d + [2 * n]
+    offs, regs, total = zdp.plan_arena(sizes, traffic, 1 << 30, region_bytes=64 << 20)
+    assert len(set(regs)) >= 2
+    arena = torch.zeros(total, dtype=torch.uint8, device=DEV)
+    master, m, v = (zdp.arena_view(arena, offs[i], n, torch.float32) for i in range(3))
+    reps_dev = [zdp.arena_view(arena, offs[3 + r], n, TORCH16[dt]) for r in range(n_d)]
+    flat = zdp.arena_view(arena, offs[3 + n_d], n, TORCH16[dt])
+    master0 = normal_f32_np(n, 0.02, (24, "master"))
+    flat0 = to16_bits_np(master0, dt)
+    master.copy_(up32(master0))
+    flat.copy_(up16(flat0, dt))
+    ws, st = zdp.new_workspace(1), zdp.new_state(1.0)
+    og = oracle.Group(replicas=None, grad_dt=odt, master=master0.copy(), m=np.zeros(n, np.float32),
+                      v=np.zeros(n, np.float32), param=flat0.copy(), param_dt=odt, weight_decay=0.1)
+    ost = oracle.State()
+    for k in range(steps):
+        reps = [grads16_np(n, dt, 1.0, (24, k, r)) for r in range(n_d)]
+        for d, b in zip(reps_dev, reps):
+            d.copy_(up16(b, dt))
+        zdp.adam_step([zdp.Group(master, m, v, replicas=reps_dev, flat_param=flat, weight_decay=0.1)], ws, st)
+        og.replicas = reps
+        oracle.step([og], oracle.Policy(), ost)
+    torch.cuda.synchronize()
+    _compare_group("arena", master, m, v, og)
+    _compare_state("arena", st, ost)
+    assert_u16_equal(down16(flat), og.param, "arena param")

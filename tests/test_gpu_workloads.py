@@ -20,6 +20,7 @@ import torch
 
 import oracle
 import zero_dp_partitioned_amd as zdp
+from zero_dp_partitioned_amd import layout
 from workloads import WORKLOADS, derive_seed, fill_normal_, torch_dtype
 
 from _gpu_helpers import DEV, ORACLE_DT, assert_bits_equal, assert_u16_equal, down16, down32
@@ -75,7 +76,8 @@ def _sample(n, boundaries, seed, k=4096):
 
 
 class Run:
-    """Device buffers of a workload (laid out as bench.py lays them out) and the
+    """Device buffers of a workload (laid out as bench.py lays them out: one
+    arena over HBM's regions, gradient copies as a pointer table) and the
     oracle's copy of the sampled coordinates."""
 
     def __init__(self, key, full=False, optimistic=False):
@@ -85,26 +87,29 @@ class Run:
         gdt, pdt = torch_dtype(wl.grad_dt), torch_dtype(wl.param_dt)
         self.odt = ORACLE_DT[wl.grad_dt]
         self.groups, self.ogroups, self.samples, self.outside = [], [], [], []
-        for gi, spec in enumerate(wl.groups):
+        shards = []
+        for spec in wl.groups:
             psi = sum(spec.numels)
             segs, _ = zdp.partition(psi, wl.n_d)
-            off, n = segs[wl.rank]
             o_off, o_size, _ = oracle.partition(psi, wl.n_d)
-            assert (off, n) == (int(o_off[wl.rank]), int(o_size[wl.rank]))
-            master = torch.empty(n, dtype=torch.float32, device=DEV)
+            assert segs[wl.rank] == (int(o_off[wl.rank]), int(o_size[wl.rank]))
+            shards.append((psi, *segs[wl.rank]))
+        pipeline = ("optimistic" if optimistic else "checked") if wl.dynamic_loss_scale else "fused"
+        specs = layout.step_specs(shards, wl.n_d, gdt, pdt, pipeline, wl.n_d <= layout.INLINE_COPIES)
+        buf, self.placement = layout.allocate(specs, DEV, "regions")
+        print(f"  layout: {self.placement}", flush=True)
+        for gi, (spec, (psi, off, n)) in enumerate(zip(wl.groups, shards)):
+            master = buf[(gi, "master")][:n]
             fill_normal_(master, 0.02, derive_seed(wl.key, gi, "master"))
-            flat = torch.empty(psi, dtype=pdt, device=DEV)
+            flat = buf[(gi, "flat")][:psi]
             fill_normal_(flat, 0.02, derive_seed(wl.key, gi, "flat"))
             flat[off:off + n].copy_(master)
-            stride = ((n + 63) // 64) * 64
-            gbuf = torch.empty(max(1, wl.n_d * stride), dtype=gdt, device=DEV)
-            reps = [gbuf[r * stride:r * stride + n] for r in range(wl.n_d)]
+            reps = layout.copies_of(buf, gi, wl.n_d, n)
             alt = {}
             if optimistic:
-                alt = dict(master_alt=torch.empty_like(master), exp_avg_alt=torch.empty_like(master),
-                           exp_avg_sq_alt=torch.empty_like(master))
-            self.groups.append(zdp.Group(master=master, exp_avg=torch.zeros_like(master),
-                                         exp_avg_sq=torch.zeros_like(master), replicas=reps,
+                alt = {name: buf[(gi, name)][:n] for name in ("master_alt", "exp_avg_alt", "exp_avg_sq_alt")}
+            self.groups.append(zdp.Group(master=master, exp_avg=buf[(gi, "exp_avg")][:n].zero_(),
+                                         exp_avg_sq=buf[(gi, "exp_avg_sq")][:n].zero_(), replicas=reps,
                                          flat_param=flat, param_offset=off, lr=wl.lr, beta1=wl.beta1,
                                          beta2=wl.beta2, eps=wl.eps, weight_decay=spec.weight_decay, **alt))
             # sample: tensor boundaries inside the shard, the middle (inf site)
@@ -126,7 +131,8 @@ class Run:
         self.ostate = oracle.State(loss_scale=wl.loss_scale)
         self.policy = oracle.Policy(skip_on_overflow=wl.dynamic_loss_scale)
         self.policy_ = zdp.policy(True, optimistic=optimistic) if wl.dynamic_loss_scale else None
-        self.avg = [torch.empty_like(g.master) for g in self.groups] if wl.dynamic_loss_scale else None
+        self.avg = ([buf[(gi, "avg")][:g.master.numel()] for gi, g in enumerate(self.groups)]
+                    if pipeline == "checked" else None)
 
     def draw_grads(self, call):
         wl = self.wl

@@ -23,10 +23,12 @@ MAX_GROUPS = 8
 MAX_REPLICAS = 4096
 DT_F16 = 1
 DT_BF16 = 2
+HBM_REGION_BYTES = 96 << 30
+ARENA_ALIGN = 2 << 20
 
 EXPORTS = ("zero_partition", "zero_partition_tensors", "zero_workspace_bytes",
            "zero_last_error", "zero_state_init", "zero_reduce_grad_segment",
-           "zero_grad_norm_overflow", "zero_adam_step", "zero_cast_writeback")
+           "zero_grad_norm_overflow", "zero_adam_step", "zero_cast_writeback", "zero_plan_arena")
 
 
 class ZeroError(RuntimeError):
@@ -43,6 +45,11 @@ class TensorSlice(ctypes.Structure):
     _fields_ = [("tensor", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("shard_begin", ctypes.c_int64), ("tensor_begin", ctypes.c_int64),
                 ("length", ctypes.c_int64)]
+
+
+class ArenaBuffer(ctypes.Structure):
+    _fields_ = [("bytes", ctypes.c_int64), ("traffic", ctypes.c_int64), ("offset", ctypes.c_int64),
+                ("region", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class StepState(ctypes.Structure):
@@ -113,6 +120,7 @@ def load():
                                               ctypes.POINTER(Policy), vp, vp]
         L.zero_adam_step.argtypes = [ctypes.POINTER(_Group), i32, ctypes.POINTER(Policy), vp, sz, vp, vp]
         L.zero_cast_writeback.argtypes = [vp, i64, vp, i64, i32, vp]
+        L.zero_plan_arena.argtypes = [ctypes.POINTER(ArenaBuffer), i32, i64, i32, i64, ctypes.POINTER(i64)]
         for name in EXPORTS:
             fn = getattr(L, name)
             if name not in ("zero_workspace_bytes", "zero_last_error"):
@@ -156,6 +164,29 @@ def partition_tensors(numels, n_d, rank, align_elems=1):
 
 def workspace_bytes(n_groups):
     return int(load().zero_workspace_bytes(n_groups))
+
+
+def plan_arena(sizes, traffic, max_bytes, region_bytes=0, n_regions=0):
+    """Offsets of buffers of `sizes` bytes, moving `traffic` bytes per step, in
+    one arena of at most `max_bytes`: ([offset], [region], arena_bytes)."""
+    if len(sizes) != len(traffic):
+        raise ValueError("sizes and traffic differ in length")
+    arr = (ArenaBuffer * max(1, len(sizes)))()
+    for i, (b, t) in enumerate(zip(sizes, traffic)):
+        arr[i].bytes, arr[i].traffic = int(b), int(t)
+    total = ctypes.c_int64(0)
+    _check(load().zero_plan_arena(arr, len(sizes), int(region_bytes), int(n_regions), int(max_bytes),
+                                  ctypes.byref(total)))
+    return [arr[i].offset for i in range(len(sizes))], [arr[i].region for i in range(len(sizes))], total.value
+
+
+def arena_view(arena, offset, numel, dtype):
+    """A `numel`-element view of dtype at byte `offset` of a uint8 arena tensor."""
+    torch = _torch()
+    nbytes = numel * torch.empty((), dtype=dtype).element_size()
+    if offset < 0 or offset + nbytes > arena.numel():
+        raise ValueError("view outside the arena")
+    return arena[offset:offset + nbytes].view(dtype)
 
 
 # --------------------------------------------------------------------------

@@ -5,7 +5,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
+#include <vector>
 #include <unordered_map>
 
 #include "zero_dp_internal.h"
@@ -208,6 +210,77 @@ int zero_partition_tensors(const int64_t* numels, int32_t n_tensors, int32_t n_d
     ++count;
   }
   *n_out = count;
+  return ZERO_OK;
+}
+
+int zero_plan_arena(zero_arena_buffer* buffers, int32_t n_buffers, int64_t region_bytes,
+                    int32_t n_regions, int64_t max_bytes, int64_t* arena_bytes) {
+  constexpr int32_t kMaxRegions = 16;
+  const int64_t A = ZERO_ARENA_ALIGN;
+  if (!buffers || n_buffers < 1) return fail(ZERO_ERR_INVALID_ARG, "no buffers");
+  if (!arena_bytes) return fail(ZERO_ERR_INVALID_ARG, "arena_bytes is NULL");
+  if (region_bytes == 0) region_bytes = ZERO_HBM_REGION_BYTES;
+  if (region_bytes < A || region_bytes % A)
+    return fail(ZERO_ERR_INVALID_ARG, "region_bytes must be a positive multiple of %lld", (long long)A);
+  if (n_regions < 0 || n_regions > kMaxRegions)
+    return fail(ZERO_ERR_INVALID_ARG, "n_regions = %d outside [0, %d]", n_regions, kMaxRegions);
+  if (max_bytes < A) return fail(ZERO_ERR_INVALID_ARG, "max_bytes below one alignment unit");
+  std::vector<int64_t> size(n_buffers);
+  for (int32_t i = 0; i < n_buffers; ++i) {
+    if (buffers[i].bytes < 1) return fail(ZERO_ERR_INVALID_ARG, "buffers[%d].bytes < 1", i);
+    if (buffers[i].traffic < 0) return fail(ZERO_ERR_INVALID_ARG, "buffers[%d].traffic < 0", i);
+    if (buffers[i].bytes > INT64_MAX - A) return fail(ZERO_ERR_INVALID_ARG, "buffers[%d].bytes too large", i);
+    size[i] = (buffers[i].bytes + A - 1) / A * A;
+  }
+  // heaviest traffic first; ties: larger first, then lower index
+  std::vector<int32_t> order(n_buffers);
+  for (int32_t i = 0; i < n_buffers; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+    if (buffers[a].traffic != buffers[b].traffic) return buffers[a].traffic > buffers[b].traffic;
+    return size[a] > size[b];
+  });
+  std::vector<int64_t> off(n_buffers);
+  std::vector<int32_t> reg(n_buffers);
+  auto place = [&](int32_t regions) -> bool {
+    std::vector<int64_t> cap(regions), used(regions, 0), load(regions, 0);
+    for (int32_t r = 0; r < regions; ++r) {
+      const int64_t start = static_cast<int64_t>(r) * region_bytes;
+      const int64_t room = start < max_bytes ? (max_bytes - start) / A * A : 0;
+      cap[r] = room < region_bytes ? room : region_bytes;
+    }
+    for (int32_t i : order) {
+      int32_t best = -1;
+      for (int32_t r = 0; r < regions; ++r)
+        if (size[i] <= cap[r] - used[r] && (best < 0 || load[r] < load[best])) best = r;
+      if (best < 0) return false;
+      reg[i] = best;
+      off[i] = static_cast<int64_t>(best) * region_bytes + used[best];
+      used[best] += size[i];
+      load[best] += buffers[i].traffic;
+    }
+    return true;
+  };
+  bool ok = false;
+  if (n_regions > 0) {
+    if (static_cast<int64_t>(n_regions - 1) > (max_bytes - 1) / region_bytes)
+      return fail(ZERO_ERR_UNSUPPORTED, "%d regions of %lld bytes do not start below max_bytes = %lld",
+                  n_regions, (long long)region_bytes, (long long)max_bytes);
+    ok = place(n_regions);
+  } else {
+    // the fewest regions, at least two where max_bytes allows, that hold every buffer
+    const int64_t avail = (max_bytes - 1) / region_bytes + 1;
+    const int32_t most = static_cast<int32_t>(avail < kMaxRegions ? avail : kMaxRegions);
+    for (int32_t r = most >= 2 ? 2 : 1; r <= most && !ok; ++r) ok = place(r);
+  }
+  if (!ok) return fail(ZERO_ERR_UNSUPPORTED, "the buffers do not fit in the regions below max_bytes");
+  int64_t end = 0;
+  for (int32_t i = 0; i < n_buffers; ++i) {
+    buffers[i].offset = off[i];
+    buffers[i].region = reg[i];
+    buffers[i].reserved = 0;
+    end = std::max(end, off[i] + size[i]);
+  }
+  *arena_bytes = end;
   return ZERO_OK;
 }
 

@@ -1,0 +1,97 @@
+"""Device buffers of one rank's step, laid out in HBM.
+
+A step streams every buffer once: the N_d 16-bit gradient copies are read,
+fp32 master / exp_avg / exp_avg_sq are read and written (or, in the
+optimistic pipeline, one state set is read and the other written), an fp32
+average is written and read back (checked pipeline), and the rank's slice of
+the 16-bit flat parameter vector is written.
+
+placement "regions": one arena, allocated before anything else large, with
+every buffer at the offset zero_plan_arena gives, so that the step's traffic
+spreads over MI355X's 96 GiB HBM regions (the region helper in the C ABI says
+why). placement "packed": one allocation per buffer in order, which on a fresh
+device puts a small shard's buffers side by side in one region.
+
+Only marshalling happens here: the plan comes from the C library and the
+arena is an ordinary torch allocation.
+"""
+from dataclasses import dataclass
+
+from . import arena_view, plan_arena
+
+PLACEMENTS = ("regions", "packed")
+INLINE_COPIES = 64  # gradient copies the kernels take as a pointer table
+SMALL_STEP_BYTES = 1 << 30
+
+
+@dataclass
+class BufferSpec:
+    key: tuple      # (group, name) or (group, "grad", r)
+    numel: int
+    dtype: object   # torch dtype
+    traffic: int    # bytes a step moves through the buffer
+
+
+def step_specs(shards, n_d, grad_dtype, param_dtype, pipeline, copies_as_table):
+    """Buffers of a step over groups `shards` = [(psi, offset, n)]:
+    pipeline "fused", "checked" (adds an fp32 average) or "optimistic" (adds a
+    second state set). The gradient copies of a group are separate buffers
+    when copies_as_table (N_d <= 64), else one buffer of N_d copies spaced by n
+    rounded up to 64 elements (key (g, "gradbuf"))."""
+    import torch
+    f32 = torch.float32
+    out = []
+    for gi, (psi, _, n) in enumerate(shards):
+        state = 4 * n if pipeline == "optimistic" else 8 * n
+        for name in ("master", "exp_avg", "exp_avg_sq"):
+            out.append(BufferSpec((gi, name), n, f32, state))
+        if pipeline == "optimistic":
+            for name in ("master_alt", "exp_avg_alt", "exp_avg_sq_alt"):
+                out.append(BufferSpec((gi, name), n, f32, 4 * n))
+        if pipeline == "checked":
+            out.append(BufferSpec((gi, "avg"), n, f32, 8 * n))
+        if copies_as_table:
+            for r in range(n_d):
+                out.append(BufferSpec((gi, "grad", r), n, grad_dtype, 2 * n))
+        else:
+            out.append(BufferSpec((gi, "gradbuf"), n_d * copy_stride(n), grad_dtype, 2 * n * n_d))
+        out.append(BufferSpec((gi, "flat"), psi, param_dtype, 2 * n))
+    return out
+
+
+def copy_stride(n):
+    """Elements between gradient copies in one shared buffer."""
+    return (n + 63) // 64 * 64
+
+
+def allocate(specs, device, placement="regions", reserve_bytes=4 << 30):
+    """({key: tensor}, info) for `specs`. "regions" leaves `reserve_bytes` of
+    the free memory outside the arena for everything else."""
+    import torch
+    if placement not in PLACEMENTS:
+        raise ValueError(f"unknown placement {placement!r}")
+    sizes = [max(1, s.numel) * torch.empty((), dtype=s.dtype).element_size() for s in specs]
+    bufs = {}
+    info = {"placement": placement}
+    if placement == "regions":
+        free, _ = torch.cuda.mem_get_info(device)
+        # a step under SMALL_STEP_BYTES is bound by launch latency, not HBM: one region
+        n_regions = 1 if sum(sizes) < SMALL_STEP_BYTES else 0
+        offs, regs, total = plan_arena(sizes, [s.traffic for s in specs], free - reserve_bytes,
+                                       n_regions=n_regions)
+        arena = torch.empty(total, dtype=torch.uint8, device=device)
+        for s, o in zip(specs, offs):
+            bufs[s.key] = arena_view(arena, o, max(1, s.numel), s.dtype)
+        info.update(arena_bytes=total, regions=len(set(regs)))
+    else:
+        for s in specs:
+            bufs[s.key] = torch.empty(max(1, s.numel), dtype=s.dtype, device=device)
+    return bufs, info
+
+
+def copies_of(bufs, gi, n_d, n):
+    """The N_d gradient copy views of group gi."""
+    if (gi, "gradbuf") in bufs:
+        b, stride = bufs[(gi, "gradbuf")], copy_stride(n)
+        return [b[r * stride:r * stride + n] for r in range(n_d)]
+    return [bufs[(gi, "grad", r)][:n] for r in range(n_d)]
