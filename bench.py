@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--pipeline", choices=["checked", "optimistic"], default="checked",
                    help="dynamic-loss-scale workloads: verdict before the update (checked) or an "
                         "update into a second state set committed afterwards (optimistic)")
+    p.add_argument("--arena", choices=["whole", "sized"], default="whole",
+                   help="regions placement: the arena is all free memory but 4 GiB (whole) or ends "
+                        "at the last planned buffer (sized)")
     p.add_argument("--placement", choices=["regions", "packed"], default="regions",
                    help="buffers carved from one arena spread over HBM's 96 GiB regions (regions), or "
                         "one allocation each in order (packed)")
@@ -81,10 +84,11 @@ class Setup:
     (zero), the N_d 16-bit gradient copies of the shard, and the group's whole
     16-bit flat parameter vector (plus a second state set for the optimistic
     pipeline, or an fp32 average for the checked one), placed by
-    zero_dp_partitioned_amd.layout: "regions" (one arena spread over HBM's
-    96 GiB regions, the default) or "packed" (one allocation per buffer)."""
+    zero_dp_partitioned_amd.layout: "regions" (one arena over all free HBM,
+    buffers spread over its 96 GiB regions; the default) or "packed" (one
+    allocation per buffer)."""
 
-    def __init__(self, wl, dev, optimistic=False, placement="regions"):
+    def __init__(self, wl, dev, optimistic=False, placement="regions", whole=True):
         import zero_dp_partitioned_amd as zdp
         from zero_dp_partitioned_amd import layout
         from workloads import derive_seed, fill_normal_, torch_dtype
@@ -102,7 +106,7 @@ class Setup:
         table = placement == "regions" and wl.n_d <= layout.INLINE_COPIES
         specs = layout.step_specs(shards, wl.n_d, torch_dtype(wl.grad_dt), torch_dtype(wl.param_dt),
                                   pipeline, table)
-        buf, self.placement = layout.allocate(specs, dev, placement)
+        buf, self.placement = layout.allocate(specs, dev, placement, whole=whole)
         for gi, (spec, (psi, off, n)) in enumerate(zip(wl.groups, shards)):
             master = buf[(gi, "master")][:n]
             fill_normal_(master, 0.02, derive_seed(wl.key, gi, "master"))
@@ -196,7 +200,8 @@ def main():
     torch.cuda.set_device(dev)
     wl = WORKLOADS[args.workload]
     log(args, f"workload {wl.key}: {wl.title}")
-    setup = Setup(wl, dev, optimistic=args.pipeline == "optimistic", placement=args.placement)
+    setup = Setup(wl, dev, optimistic=args.pipeline == "optimistic", placement=args.placement,
+                  whole=args.arena == "whole")
     S = setup.shard
     bpp = bytes_per_param(wl.n_d)
     log(args, f"shard {S} params, {len(setup.groups)} group(s), {bpp} B/param, "

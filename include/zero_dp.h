@@ -191,11 +191,13 @@ size_t zero_workspace_bytes(int32_t n_groups);
  * when every stream of a step lies in one region the step sustains about
  * 5.4 TB/s; with its traffic spread over two or more regions about 6.4 TB/s.
  * HIP exposes no physical addresses, so the helper plans byte offsets inside
- * one arena that the caller allocates in a single piece, first, on an
- * otherwise idle device: such an allocation is backed in address order, so
- * offset ranges of the arena fall into the regions (to within the few MiB the
- * runtime holds below it). The rest of each region stays free for the
- * caller's other data (weights, activations). */
+ * one arena that the caller allocates in a single piece, first, taking all
+ * free device memory but a small reserve: such an allocation is backed across
+ * the whole of HBM in address order, so offset ranges of the arena fall into
+ * the regions (to within the few MiB the runtime holds below it). A smaller
+ * allocation is backed wherever the driver finds room and gives no such
+ * guarantee. The rest of each region stays free for the caller's other data
+ * (weights, activations). */
 #define ZERO_HBM_REGION_BYTES (96LL << 30)
 #define ZERO_ARENA_ALIGN (2LL << 20) /* offsets and sizes are rounded to 2 MiB */
 

@@ -6,18 +6,19 @@ optimistic pipeline, one state set is read and the other written), an fp32
 average is written and read back (checked pipeline), and the rank's slice of
 the 16-bit flat parameter vector is written.
 
-placement "regions": one arena, allocated before anything else large, with
-every buffer at the offset zero_plan_arena gives, so that the step's traffic
-spreads over MI355X's 96 GiB HBM regions (the region helper in the C ABI says
-why). placement "packed": one allocation per buffer in order, which on a fresh
-device puts a small shard's buffers side by side in one region.
+placement "regions": one arena spanning all free HBM, allocated before
+anything else large, with every buffer at the offset zero_plan_arena gives, so
+that the step's traffic spreads over MI355X's 96 GiB HBM regions (the region
+helper in the C ABI says why). placement "packed": one allocation per buffer
+in order, which typically puts a small shard's buffers side by side in one
+region.
 
 Only marshalling happens here: the plan comes from the C library and the
 arena is an ordinary torch allocation.
 """
 from dataclasses import dataclass
 
-from . import arena_view, plan_arena
+from . import ARENA_ALIGN, arena_view, plan_arena
 
 PLACEMENTS = ("regions", "packed")
 INLINE_COPIES = 64  # gradient copies the kernels take as a pointer table
@@ -64,9 +65,17 @@ def copy_stride(n):
     return (n + 63) // 64 * 64
 
 
-def allocate(specs, device, placement="regions", reserve_bytes=4 << 30):
-    """({key: tensor}, info) for `specs`. "regions" leaves `reserve_bytes` of
-    the free memory outside the arena for everything else."""
+def allocate(specs, device, placement="regions", reserve_bytes=4 << 30, whole=True):
+    """({key: tensor}, info) for `specs`.
+
+    "regions": with `whole` (the default) the arena is all free memory but
+    `reserve_bytes`: an allocation that size is backed across the whole of
+    HBM in address order, so the planned offsets fall into the physical
+    regions. A smaller arena (whole=False: up to the end of the last buffer)
+    is backed wherever the driver finds room, which can put every planned
+    region into one physical one. The space after the planned buffers stays
+    free for the caller's other data. A step under SMALL_STEP_BYTES gets a
+    small arena in one region."""
     import torch
     if placement not in PLACEMENTS:
         raise ValueError(f"unknown placement {placement!r}")
@@ -79,6 +88,8 @@ def allocate(specs, device, placement="regions", reserve_bytes=4 << 30):
         n_regions = 1 if sum(sizes) < SMALL_STEP_BYTES else 0
         offs, regs, total = plan_arena(sizes, [s.traffic for s in specs], free - reserve_bytes,
                                        n_regions=n_regions)
+        if whole and n_regions != 1:
+            total = (free - reserve_bytes) // ARENA_ALIGN * ARENA_ALIGN
         arena = torch.empty(total, dtype=torch.uint8, device=device)
         for s, o in zip(specs, offs):
             bufs[s.key] = arena_view(arena, o, max(1, s.numel), s.dtype)
