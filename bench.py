@@ -230,11 +230,13 @@ def main():
     value = S / (ms_per_step / 1e3)
     algo_bytes = S * bpp
     achieved = algo_bytes / (ev_mean / 1e3) / 1e9
+    pipeline = ("optimistic" if setup.optimistic else "checked") if wl.dynamic_loss_scale else "fused"
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
-        rec = json.load(open(TRAFFIC_FILE)).get(wl.key)
+        key = wl.key if pipeline == "fused" else f"{wl.key}:{pipeline}"
+        rec = json.load(open(TRAFFIC_FILE)).get(key)
         if rec and rec.get("kernel_source") == kernel_source_hash():
-            traffic = rec.get("bytes_per_launch")
+            traffic = rec.get("bytes_per_step")
     cpu = None
     if args.cpu_sample > 0:
         cpu = cpu_baseline(setup, args.cpu_sample, args)
@@ -254,8 +256,7 @@ def main():
         "config": {"workload": wl.key, "shard_params": S, "n_d": wl.n_d, "rank": wl.rank,
                    "groups": len(setup.groups), "grad_dtype": wl.grad_dt, "param_dtype": wl.param_dt,
                    "loss_scale": wl.loss_scale, "dynamic_loss_scale": wl.dynamic_loss_scale,
-                   "pipeline": ("optimistic" if setup.optimistic else "checked") if wl.dynamic_loss_scale
-                   else "fused",
+                   "pipeline": pipeline,
                    "bytes_per_param": bpp, **setup.placement},
         "gbps": achieved,
         "pct_peak": 100.0 * achieved / PEAK_HBM_GBPS,
