@@ -23,9 +23,14 @@
  *     host. Scalar results (norm, overflow flag, loss scale, step count) stay in
  *     the device-resident zero_step_state.
  *   - Arguments are checked on the host before anything is enqueued: a
- *     non-zero return means nothing was launched, and zero_last_error() gives a
- *     thread-local message. Numerical overflow is not an error; it is a flag.
- *     A device fault surfaces at the caller's next synchronisation.
+ *     non-zero return other than ZERO_ERR_HIP means nothing was launched, and
+ *     zero_last_error() gives a thread-local message. ZERO_ERR_HIP reports a
+ *     failed launch; launches of the same call before it stay enqueued.
+ *     Numerical overflow is not an error; it is a flag. A device fault
+ *     surfaces at the caller's next synchronisation.
+ *   - Buffer extents are the caller's to get right: the library knows
+ *     pointers, counts and offsets, not allocation sizes (for example
+ *     flat_param must hold param_offset + n elements).
  *   - Calls on different streams with disjoint buffers may run concurrently.
  *     Calls that share a workspace or a state must be ordered by the caller.
  *   - Element counts and offsets are int64 (offsets above 2^32 are normal).

@@ -55,12 +55,9 @@ int check_device() {
     hipDeviceProp_t prop;
     e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
-    const int is950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-    it = ok.emplace(dev, is950).first;
-    if (!is950) snprintf(g_err, sizeof g_err, "device %d is %s, this library is built for gfx950", dev,
-                         prop.gcnArchName);
+    it = ok.emplace(dev, strncmp(prop.gcnArchName, "gfx950", 6) == 0).first;
   }
-  if (!it->second) return ZERO_ERR_UNSUPPORTED;
+  if (!it->second) return fail(ZERO_ERR_UNSUPPORTED, "device %d is not gfx950, the target this library is built for", dev);
   return ZERO_OK;
 }
 
@@ -99,7 +96,8 @@ int check_policy(const zero_policy* p) {
 bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
 // Fill a GradSource from a host array of replica pointers. Sets *vec_ok to
-// whether every replica start is 16-byte aligned (the vector path).
+// whether every replica start is 8-byte aligned (the quad path loads four
+// 16-bit values at a time).
 // An empty shard (n == 0) reads nothing, so its pointers may be NULL.
 int make_source(const void* const* replicas, int32_t n_d, int32_t dt, int64_t n, GradSource* S, bool* vec_ok) {
   memset(S, 0, sizeof *S);
