@@ -126,3 +126,35 @@ def test_step_specs_traffic_is_the_bytes_model(pipeline, extra, n_d, table):
         assert ((gi, "gradbuf") in keys) == (not table)
         assert ((gi, "master_alt") in keys) == (pipeline == "optimistic")
         assert ((gi, "avg") in keys) == (pipeline == "checked")
+
+
+def test_free_ranges_are_the_gaps():
+    from zero_dp_partitioned_amd import layout
+    MiB = 1 << 20
+    assert A == 2 * MiB
+    # buffers at 0 (3 MiB), 20 MiB (1 byte), 40 MiB (4 MiB) in a 60 MiB arena: each gap starts at the
+    # next 2 MiB boundary after a buffer's end
+    offs, sizes, total = [0, 20 * MiB, 40 * MiB], [3 * MiB, 1, 4 * MiB], 60 * MiB
+    assert layout.free_ranges(offs, sizes, total) == [(4 * MiB, 16 * MiB), (22 * MiB, 18 * MiB),
+                                                      (44 * MiB, 16 * MiB)]
+    # unsorted input, touching buffers, a tail shorter than the alignment
+    assert layout.free_ranges([4 * MiB, 0], [4 * MiB, 4 * MiB], 8 * MiB + 1) == []
+    assert layout.free_ranges([0], [1], 1) == []
+
+
+@settings(max_examples=200, deadline=None)
+@given(items=st.lists(st.tuples(st.integers(1, 40 << 20), st.integers(0, 100)), min_size=1, max_size=16),
+       n_regions=st.integers(1, 4))
+def test_free_ranges_cover_the_rest_of_a_plan(items, n_regions):
+    from zero_dp_partitioned_amd import layout
+    region = 1 << 30
+    sizes = [s for s, _ in items]
+    offs, regs, total = zdp.plan_arena(sizes, [t for _, t in items], n_regions * region,
+                                      region_bytes=region, n_regions=n_regions)
+    free = layout.free_ranges(offs, sizes, total)
+    used = [(o, o + _up(b)) for o, b in zip(offs, sizes)]
+    for fo, fb in free:
+        assert fo % A == 0 and fb % A == 0 and fb >= A
+        assert all(fo + fb <= lo or hi <= fo for lo, hi in used), "free range overlaps a buffer"
+    # buffers plus free ranges account for the whole arena (plans are aligned)
+    assert sum(_up(b) for b in sizes) + sum(fb for _, fb in free) == total

@@ -66,7 +66,9 @@ def copy_stride(n):
 
 
 def allocate(specs, device, placement="regions", reserve_bytes=4 << 30, whole=True):
-    """({key: tensor}, info) for `specs`.
+    """({key: tensor}, info) for `specs`. With "regions" the dict also holds
+    "arena" (the uint8 arena) and "free" (its unused (offset, bytes) ranges,
+    see free_ranges) for carving the caller's other tensors with arena_view.
 
     "regions": with `whole` (the default) the arena is all free memory but
     `reserve_bytes`: an allocation that size is backed across the whole of
@@ -94,10 +96,27 @@ def allocate(specs, device, placement="regions", reserve_bytes=4 << 30, whole=Tr
         for s, o in zip(specs, offs):
             bufs[s.key] = arena_view(arena, o, max(1, s.numel), s.dtype)
         info.update(arena_bytes=total, regions=len(set(regs)))
+        # the arena itself and its unused byte ranges, for the caller's other data
+        bufs["arena"] = arena
+        bufs["free"] = free_ranges(offs, sizes, total)
     else:
         for s in specs:
             bufs[s.key] = torch.empty(max(1, s.numel), dtype=s.dtype, device=device)
     return bufs, info
+
+
+def free_ranges(offsets, sizes, total):
+    """[(offset, bytes)] of the ARENA_ALIGN-aligned gaps of at least
+    ARENA_ALIGN bytes that buffers at `offsets` of `sizes` leave in an arena
+    of `total` bytes, in address order."""
+    spans = sorted((o, o + s) for o, s in zip(offsets, sizes))
+    out, at = [], 0
+    for lo, hi in spans + [(total, total)]:
+        start = (at + ARENA_ALIGN - 1) // ARENA_ALIGN * ARENA_ALIGN
+        if lo - start >= ARENA_ALIGN:
+            out.append((start, (lo - start) // ARENA_ALIGN * ARENA_ALIGN))
+        at = max(at, hi)
+    return out
 
 
 def copies_of(bufs, gi, n_d, n):
