@@ -2,10 +2,11 @@
  * A plain C consumer of the zero_dp C ABI: no torch, no Python.
  *
  * Lays out one rank's shard the way a training loop would (rank `rank` of
- * `n_d` over a flat fp16 vector of `psi` elements), fills the inputs from a
- * fixed integer recipe, runs `steps` fused steps on the null stream, and
- * writes the inputs and results to a binary file for the test to check
- * against the CPU oracle:
+ * `n_d` over a flat fp16 vector of `psi` elements), places its buffers in one
+ * hipMalloc'd arena at the offsets zero_plan_arena gives (64 MiB regions, so
+ * the arena stays small), fills the inputs from a fixed integer recipe, runs
+ * `steps` fused steps on the null stream, and writes the inputs and results
+ * to a binary file for the test to check against the CPU oracle:
  *
  *   step_demo OUT PSI N_D RANK STEPS
  *
@@ -91,16 +92,27 @@ int main(int argc, char** argv) {
       for (int64_t j = 0; j < n; ++j)
         reps[(k * n_d + r) * n + j] = grad_bits(((uint64_t)k << 48) ^ ((uint64_t)r << 40) ^ (uint64_t)(off + j));
 
-  /* device buffers, owned here */
-  float *d_master, *d_m, *d_v;
-  uint16_t *d_flat, *d_reps;
+  /* device buffers, owned here: master, m, v, the n_d copies (one buffer) and
+   * the flat vector, carved from one arena */
+  zero_arena_buffer plan[5];
+  memset(plan, 0, sizeof plan);
+  const int64_t sizes[5] = {4 * n, 4 * n, 4 * n, 2 * n * n_d, 2 * psi};
+  const int64_t traffic[5] = {8 * n, 8 * n, 8 * n, 2 * n * n_d, 2 * n};
+  for (int i = 0; i < 5; ++i) {
+    plan[i].bytes = sizes[i] > 0 ? sizes[i] : 1;
+    plan[i].traffic = traffic[i];
+  }
+  int64_t arena_bytes = 0;
+  ZERO_OK_OR_DIE(zero_plan_arena(plan, 5, 64LL << 20, 0, 1LL << 30, &arena_bytes));
+  char* d_arena;
+  HIP_OK(hipMalloc((void**)&d_arena, (size_t)arena_bytes));
+  float* d_master = (float*)(d_arena + plan[0].offset);
+  float* d_m = (float*)(d_arena + plan[1].offset);
+  float* d_v = (float*)(d_arena + plan[2].offset);
+  uint16_t* d_reps = (uint16_t*)(d_arena + plan[3].offset);
+  uint16_t* d_flat = (uint16_t*)(d_arena + plan[4].offset);
   void *d_ws, *d_state;
   const size_t ws_bytes = zero_workspace_bytes(1);
-  HIP_OK(hipMalloc((void**)&d_master, sizeof(float) * (size_t)n));
-  HIP_OK(hipMalloc((void**)&d_m, sizeof(float) * (size_t)n));
-  HIP_OK(hipMalloc((void**)&d_v, sizeof(float) * (size_t)n));
-  HIP_OK(hipMalloc((void**)&d_flat, sizeof(uint16_t) * (size_t)psi));
-  HIP_OK(hipMalloc((void**)&d_reps, sizeof(uint16_t) * (size_t)(n_d * n)));
   HIP_OK(hipMalloc(&d_ws, ws_bytes));
   HIP_OK(hipMalloc(&d_state, sizeof(zero_step_state)));
   HIP_OK(hipMemcpy(d_master, master0, sizeof(float) * (size_t)n, hipMemcpyHostToDevice));
@@ -159,14 +171,13 @@ int main(int argc, char** argv) {
   fwrite(&st.grad_norm_sq, sizeof(double), 1, f);
   fwrite(&st.step, sizeof(int64_t), 1, f);
   fclose(f);
-  printf("step_demo: psi=%lld n_d=%d rank=%d offset=%lld n=%lld steps=%lld norm=%g\n", (long long)psi, n_d,
-         rank, (long long)off, (long long)n, (long long)steps, (double)st.grad_norm);
+  printf("step_demo: psi=%lld n_d=%d rank=%d offset=%lld n=%lld steps=%lld norm=%g arena=%lld bytes, regions",
+         (long long)psi, n_d, rank, (long long)off, (long long)n, (long long)steps, (double)st.grad_norm,
+         (long long)arena_bytes);
+  for (int i = 0; i < 5; ++i) printf(" %d", plan[i].region);
+  printf("\n");
 
-  hipFree(d_master);
-  hipFree(d_m);
-  hipFree(d_v);
-  hipFree(d_flat);
-  hipFree(d_reps);
+  hipFree(d_arena);
   hipFree(d_ws);
   hipFree(d_state);
   free(flat0);
