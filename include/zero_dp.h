@@ -96,7 +96,9 @@ typedef struct {
   float clip_coef;      /* last step: gradient-clipping multiplier (1 = none)  */
   int32_t cur;          /* optimistic pipeline: 0 = master/exp_avg/exp_avg_sq
                            hold the current state, 1 = the *_alt arrays do    */
-  int32_t reserved;
+  int32_t redo;         /* optimistic pipeline with clipping: 1 between the
+                           norm and the second pass of a clipped step (0 once
+                           zero_adam_step's work has run)                    */
 } zero_step_state;
 
 /* Step policy: loss scaling and gradient clipping.
@@ -110,9 +112,10 @@ typedef struct {
  *   [DeepSpeed walkthrough §6 step 3 "unscale and clip"]: multiplier
  *   c = min(1, max_norm / (norm + 1e-6)) formed in fp64 and rounded once to
  *   fp32, g <- (avg * (1/S)) * c; 0 = no clipping.
- * optimistic = 1 (with skip_on_overflow = 1, without clipping): instead of
- *   waiting for the overflow verdict, update into a second state set and
- *   commit or discard it afterwards (see zero_adam_step).
+ * optimistic = 1 (with skip_on_overflow = 1): instead of waiting for the
+ *   overflow verdict and the norm, update into a second state set and commit
+ *   or discard it afterwards; a step the norm says to clip is recomputed from
+ *   the current set by a second pass (see zero_adam_step).
  * Skipping or clipping without `optimistic` needs the norm before the update
  * and selects the checked pipeline. */
 typedef struct {
@@ -289,16 +292,20 @@ int zero_grad_norm_overflow(const void* const* grads, const int64_t* counts, int
  *     the loss scale changes; otherwise the update is applied with g
  *     multiplied by state->clip_coef, and the step advances. Scale
  *     backoff/growth happen here.
- *   - "optimistic" (skip_on_overflow 1, optimistic 1, no clipping): one pass
- *     per group reads the current set (state->cur), writes the updated values
- *     into the other set and into flat_param, and emits norm partials; then
- *     without overflow the other set becomes current (cur flips) and the step
+ *   - "optimistic" (skip_on_overflow 1, optimistic 1): one pass per group
+ *     reads the current set (state->cur), writes the updated values into the
+ *     other set and into flat_param, and emits norm partials; then without
+ *     overflow the other set becomes current (cur flips) and the step
  *     advances; with overflow the current set stays, the scale backs off, and
  *     flat_param's slice is rewritten from the current master. That restores
  *     it exactly when the slice held RNE16(current master) before the step,
- *     as it does after zero_cast_writeback() or any applied step. Costs a
- *     second state set (12 B/param) instead of the checked pipeline's extra
- *     pass over an fp32 average.
+ *     as it does after zero_cast_writeback() or any applied step. With
+ *     max_grad_norm > 0, a step whose norm asks for clipping (multiplier < 1)
+ *     is recomputed by a second pass from the current set with the
+ *     multiplier, then committed: the result is the checked pipeline's, and
+ *     steps that need no clipping stay one pass. Costs a second state set
+ *     (12 B/param) instead of the checked pipeline's extra pass over an fp32
+ *     average.
  * `groups` is a host array; group g uses workspace slot g and the beta powers
  * state->beta*_pow[g].
  * Errors: INVALID_ARG, ALIGNMENT, WORKSPACE, UNSUPPORTED. */

@@ -140,14 +140,15 @@ def test_device_calls_reject_bad_arguments_before_launch():
         assert L.zero_adam_step(garr, 1, ctypes.byref(badclip), fake, W, fake, None) == zdp.ERR_INVALID_ARG
         assert L.zero_grad_norm_overflow(None, None, 1, 1, fake, W, ctypes.byref(badclip), fake,
                                          None) == zdp.ERR_INVALID_ARG
-    # optimistic needs skip, no clipping, and the second state set
-    for pol in (zdp.policy(False, optimistic=True), zdp.policy(True, optimistic=True, max_grad_norm=1.0)):
-        assert L.zero_adam_step(garr, 1, ctypes.byref(pol), fake, W, fake, None) == zdp.ERR_INVALID_ARG
-    opt = zdp.policy(True, optimistic=True)
+    # optimistic needs skip and the second state set (with or without clipping)
+    pol = zdp.policy(False, optimistic=True)
+    assert L.zero_adam_step(garr, 1, ctypes.byref(pol), fake, W, fake, None) == zdp.ERR_INVALID_ARG
+    assert "skip_on_overflow" in zdp.last_error()
     g.beta1 = 0.9
     garr = (zdp._Group * 1)(g)
-    assert L.zero_adam_step(garr, 1, ctypes.byref(opt), fake, W, fake, None) == zdp.ERR_INVALID_ARG
-    assert "_alt" in zdp.last_error()
+    for opt in (zdp.policy(True, optimistic=True), zdp.policy(True, optimistic=True, max_grad_norm=1.0)):
+        assert L.zero_adam_step(garr, 1, ctypes.byref(opt), fake, W, fake, None) == zdp.ERR_INVALID_ARG
+        assert "_alt" in zdp.last_error()
     # a workspace smaller than zero_workspace_bytes()
     g.beta1 = 0.9
     garr2 = (zdp._Group * 2)(g, g)

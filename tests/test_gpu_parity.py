@@ -543,3 +543,57 @@ def test_fused_step_in_a_planned_arena():
     _compare_group("arena", master, m, v, og)
     _compare_state("arena", st, ost)
     assert_u16_equal(down16(flat), og.param, "arena param")
+
+
+# --------------------------------------------------------------------------
+# optimistic pipeline with clipping: one pass, a second one only for steps the
+# norm says to clip; the results are the checked pipeline's (the oracle's)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("sizes,n_d,dt", [((30_011,), 4, "f16"), ((20_000, 4_099), 2, "bf16"), ((9_001,), 1, "f16")])
+def test_optimistic_pipeline_with_clipping(sizes, n_d, dt):
+    tag = f"optimistic+clip sizes={sizes} n_d={n_d} {dt}"
+    print(f"[case] {tag}", flush=True)
+    odt = ORACLE_DT[dt]
+    total = sum(sizes)
+    max_norm = 1e-3 * np.sqrt(total / n_d)            # about the norm of an unscaled draw
+    pol = oracle.Policy(skip_on_overflow=True, growth_interval=3, max_grad_norm=max_norm)
+    sc = zdp.policy(True, growth_interval=3, max_grad_norm=max_norm, optimistic=True)
+    grps, ogs, flats0 = [], [], []
+    for gi, n in enumerate(sizes):
+        master0 = normal_f32_np(n, 0.02, (25, gi, "master"))
+        flat0 = to16_bits_np(master0, dt)
+        flats0.append(flat0)
+        grps.append(zdp.Group(up32(master0), torch.zeros(n, device=DEV), torch.zeros(n, device=DEV),
+                              master_alt=torch.empty(n, device=DEV), exp_avg_alt=torch.empty(n, device=DEV),
+                              exp_avg_sq_alt=torch.empty(n, device=DEV), flat_param=up16(flat0, dt),
+                              weight_decay=0.1 * gi))
+        ogs.append(oracle.Group(replicas=None, grad_dt=odt, master=master0.copy(), m=np.zeros(n, np.float32),
+                                v=np.zeros(n, np.float32), param=flat0.copy(), param_dt=odt,
+                                weight_decay=0.1 * gi))
+    ws, st = zdp.new_workspace(len(sizes)), zdp.new_state(1024.0)
+    ost = oracle.State(loss_scale=1024.0)
+    factors = [2.0, 0.5, 2.0, 0.5, 2.0, 0.5, 0.5, 2.0]   # draws above / below the threshold
+    clipped = unclipped = 0
+    for k, f in enumerate(factors):
+        for gi, (g, og) in enumerate(zip(grps, ogs)):
+            reps = [grads16_np(g.master.numel(), dt, ost.loss_scale * f, (25, gi, "g", k, r)) for r in range(n_d)]
+            if k == 4 and gi == 0:
+                reps[-1] = reps[-1].copy()
+                reps[-1][7] = POS_INF[dt]                  # one overflowing call
+            g.replicas = [up16(r, dt) for r in reps]
+            og.replicas = reps
+        zdp.adam_step(grps, ws, st, sc)
+        oracle.step(ogs, pol, ost)
+        torch.cuda.synchronize()
+        s = _compare_state(f"{tag} call {k + 1}", st, ost)
+        assert s["redo"] == 0
+        for gi, (g, og) in enumerate(zip(grps, ogs)):
+            cm, cmm, cv = zdp.current_state(g, s)
+            _compare_group(f"{tag} call {k + 1} group {gi}", cm, cmm, cv, og)
+            assert_u16_equal(down16(g.flat_param), og.param, f"{tag} call {k + 1} group {gi} param")
+        if not ost.skipped:
+            clipped += ost.clip < 1.0
+            unclipped += ost.clip == 1.0
+    assert ost.step == len(factors) - 1
+    assert clipped >= 3 and unclipped >= 3, (clipped, unclipped)

@@ -64,7 +64,7 @@ class StepState(ctypes.Structure):
                 ("good_steps", ctypes.c_int32),
                 ("clip_coef", ctypes.c_float),
                 ("cur", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("redo", ctypes.c_int32)]
 
 
 class Policy(ctypes.Structure):
@@ -244,7 +244,7 @@ def read_state(state):
     return {"beta1_pow": list(s.beta1_pow), "beta2_pow": list(s.beta2_pow),
             "grad_norm_sq": s.grad_norm_sq, "grad_norm": s.grad_norm, "loss_scale": s.loss_scale,
             "step": s.step, "overflow": s.overflow, "skipped": s.skipped, "good_steps": s.good_steps,
-            "clip_coef": s.clip_coef, "cur": s.cur}
+            "clip_coef": s.clip_coef, "cur": s.cur, "redo": s.redo}
 
 
 def new_workspace(n_groups, device="cuda"):
@@ -260,8 +260,9 @@ def policy(skip_on_overflow=False, growth_interval=1000, backoff=0.5, growth=2.0
            max_grad_norm=0.0, optimistic=False):
     """Loss-scale and clipping policy. Skipping or clipping selects the checked
     pipeline (reduce_grad_segment / grad_norm_overflow before adam_step), or,
-    with optimistic=True (skip, no clipping), the optimistic pipeline, which
-    needs each group's *_alt state set."""
+    with optimistic=True (needs skip), the optimistic pipeline, which needs
+    each group's *_alt state set and, when clipping triggers, runs a second
+    pass."""
     return Policy(int(bool(skip_on_overflow)), int(growth_interval), int(bool(optimistic)), 0,
                   float(backoff), float(growth), float(min_scale), float(max_grad_norm))
 

@@ -381,8 +381,8 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_policy
   if (int rc = check_policy(policy)) return rc;
   const bool dynamic = policy && policy->skip_on_overflow;
   const bool optimistic = policy && policy->optimistic;
-  if (optimistic && (!dynamic || policy->max_grad_norm > 0.0))
-    return fail(ZERO_ERR_INVALID_ARG, "the optimistic pipeline needs skip_on_overflow and no clipping");
+  if (optimistic && !dynamic) return fail(ZERO_ERR_INVALID_ARG, "the optimistic pipeline needs skip_on_overflow");
+  const bool clip_redo = optimistic && policy->max_grad_norm > 0.0;
   const bool checked = !optimistic && policy && (policy->skip_on_overflow || policy->max_grad_norm > 0.0);
   const int mode = optimistic ? kOptimistic : (checked ? kChecked : kFused);
   AdamArgs A[ZERO_MAX_GROUPS];
@@ -475,6 +475,7 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_policy
       F.backoff = policy->backoff;
       F.growth = policy->growth;
       F.min_scale = policy->min_scale;
+      F.max_grad_norm = policy->max_grad_norm;
     }
     for (int32_t g = 0; g < n_groups; ++g) {
       F.beta1[g] = groups[g].beta1;
@@ -499,6 +500,31 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_policy
         e = launch_restore(R, rv, s);
         if (e != hipSuccess) return hip_fail(e, "restore launch");
       }
+    }
+    if (clip_redo) {
+      // a step the norm says to clip: recompute it from the current set with
+      // the multiplier (the launches exit at once otherwise), then commit it
+      for (int32_t g = 0; g < n_groups; ++g) {
+        AdamArgs a = A[g];
+        a.partials = nullptr;
+        e = launch_adam(a, src[g], vec[g], kRedo, s);
+        if (e != hipSuccess) return hip_fail(e, "second-pass launch");
+      }
+      CommitArgs C;
+      memset(&C, 0, sizeof C);
+      C.state = state;
+      C.n_groups = n_groups;
+      C.dynamic = 1;
+      C.growth_interval = policy->growth_interval;
+      C.backoff = policy->backoff;
+      C.growth = policy->growth;
+      C.min_scale = policy->min_scale;
+      for (int32_t g = 0; g < n_groups; ++g) {
+        C.beta1[g] = groups[g].beta1;
+        C.beta2[g] = groups[g].beta2;
+      }
+      e = launch_redo_commit(C, s);
+      if (e != hipSuccess) return hip_fail(e, "second-pass commit launch");
     }
     return ZERO_OK;
   }

@@ -243,8 +243,14 @@ __device__ __forceinline__ void write_block_partial(double s, int bad, double* o
 template <int SRC, bool VEC, int MODE>
 __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs A) {
   constexpr bool CHECKED = MODE == kChecked;
+  constexpr bool REDO = MODE == kRedo;
+  constexpr bool CLIPPED = CHECKED || REDO;      // multiplier known before the update; no partials
+  constexpr bool SWAP = MODE == kOptimistic || REDO;
   if constexpr (CHECKED) {
     if (A.state->skipped) return;
+  }
+  if constexpr (REDO) {
+    if (!A.state->redo) return;
   }
   const Scalars s = load_scalars(A);
   const float* mst_in = A.master;
@@ -253,7 +259,7 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs A) {
   float* mst_out = A.master;
   float* m_out = A.m;
   float* v_out = A.v;
-  if constexpr (MODE == kOptimistic) {
+  if constexpr (SWAP) {
     const bool alt_is_current = A.state->cur != 0;
     mst_in = alt_is_current ? A.master_alt : A.master;
     m_in = alt_is_current ? A.m_alt : A.m;
@@ -272,8 +278,8 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs A) {
   auto one = [&](int64_t j) {
     const float a = source1<SRC>(A.src, j);
     float g = a * s.inv_scale;
-    if constexpr (!CHECKED) account(a, g, sumsq, bad);
-    if constexpr (CHECKED) g = g * s.clip;
+    if constexpr (!CLIPPED) account(a, g, sumsq, bad);
+    if constexpr (CLIPPED) g = g * s.clip;
     float th = mst_in[j], m = m_in[j], v = v_in[j];
     adam1(g, th, m, v, s);
     mst_out[j] = th;
@@ -298,8 +304,8 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs A) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           float g = a[q] * s.inv_scale;
-          if constexpr (!CHECKED) account(a[q], g, sumsq, bad);
-          if constexpr (CHECKED) g = g * s.clip;
+          if constexpr (!CLIPPED) account(a[q], g, sumsq, bad);
+          if constexpr (CLIPPED) g = g * s.clip;
           adam1(g, th[q], mm[q], vv[q], s);
         }
         st_stream(reinterpret_cast<f4*>(mst_out + e), (f4){th[0], th[1], th[2], th[3]});
@@ -317,7 +323,7 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs A) {
       }
     }
   }
-  if constexpr (!CHECKED) write_block_partial(sumsq, bad, A.partials);
+  if constexpr (!CLIPPED) write_block_partial(sumsq, bad, A.partials);
 }
 
 // ------------------------------------------------------------------------
@@ -389,6 +395,31 @@ __global__ void __launch_bounds__(kBlock) fold_kernel(const FoldArgs F) {
 // One-block kernels: combine the groups' level-2 partials, state bookkeeping
 // ------------------------------------------------------------------------
 
+// An applied step: t + 1, beta powers, and (dynamic scale) the growth window.
+__device__ __forceinline__ void advance(zero_step_state* st, int n_groups, const double* beta1,
+                                        const double* beta2, bool dynamic, int growth_interval,
+                                        double growth) {
+  st->step = st->step + 1;
+  for (int g = 0; g < n_groups; ++g) {
+    st->beta1_pow[g] = st->beta1_pow[g] * beta1[g];
+    st->beta2_pow[g] = st->beta2_pow[g] * beta2[g];
+  }
+  if (dynamic) {
+    st->good_steps = st->good_steps + 1;
+    if (growth_interval > 0 && st->good_steps == growth_interval) {
+      st->loss_scale = static_cast<float>(static_cast<double>(st->loss_scale) * growth);
+      st->good_steps = 0;
+    }
+  }
+}
+
+// Clip multiplier min(1, max_norm / (norm + 1e-6)) from the fp64 norm², rounded once; 1 = none.
+__device__ __forceinline__ float clip_multiplier(double max_grad_norm, double norm_sq) {
+  if (!(max_grad_norm > 0.0) || !__builtin_isfinite(norm_sq)) return 1.0f;
+  const double c = max_grad_norm / (__builtin_sqrt(norm_sq) + 1e-6);
+  return static_cast<float>(c < 1.0 ? c : 1.0);
+}
+
 __global__ void __launch_bounds__(kBlock) finalize_kernel(const FinalizeArgs F) {
   double total = 0.0;
   for (int g = 0; g < F.n_groups; ++g) total += block_sum(F.level2[g * kFoldBlocks + threadIdx.x]);
@@ -402,14 +433,12 @@ __global__ void __launch_bounds__(kBlock) finalize_kernel(const FinalizeArgs F) 
     // static loss scale: the update was applied whatever the flag says
     st->clip_coef = 1.0f;
     st->skipped = 0;
-    st->step = st->step + 1;
-    for (int g = 0; g < F.n_groups; ++g) {
-      st->beta1_pow[g] = st->beta1_pow[g] * F.beta1[g];
-      st->beta2_pow[g] = st->beta2_pow[g] * F.beta2[g];
-    }
+    advance(st, F.n_groups, F.beta1, F.beta2, false, 0, 1.0);
   } else if (F.mode == 2) {
-    // optimistic: the update went to the other state set; keep it or drop it
+    // optimistic: the update went to the other state set; keep it, drop it, or
+    // (clipping) have the second pass redo it from the current set
     st->clip_coef = 1.0f;
+    st->redo = 0;
     if (flag) {
       st->skipped = 1;
       double sc = static_cast<double>(st->loss_scale) * F.backoff;
@@ -418,27 +447,18 @@ __global__ void __launch_bounds__(kBlock) finalize_kernel(const FinalizeArgs F) 
       st->good_steps = 0;
     } else {
       st->skipped = 0;
-      st->cur = st->cur ^ 1;
-      st->step = st->step + 1;
-      for (int g = 0; g < F.n_groups; ++g) {
-        st->beta1_pow[g] = st->beta1_pow[g] * F.beta1[g];
-        st->beta2_pow[g] = st->beta2_pow[g] * F.beta2[g];
-      }
-      st->good_steps = st->good_steps + 1;
-      if (F.growth_interval > 0 && st->good_steps == F.growth_interval) {
-        st->loss_scale = static_cast<float>(static_cast<double>(st->loss_scale) * F.growth);
-        st->good_steps = 0;
+      const float clip = clip_multiplier(F.max_grad_norm, total);
+      if (clip < 1.0f) {
+        st->clip_coef = clip;
+        st->redo = 1;  // redo_commit_kernel flips and advances after the second pass
+      } else {
+        st->cur = st->cur ^ 1;
+        advance(st, F.n_groups, F.beta1, F.beta2, true, F.growth_interval, F.growth);
       }
     }
   } else {
     st->skipped = (flag && F.skip_on_overflow) ? 1 : 0;
-    // clip multiplier min(1, max_norm / (norm + 1e-6)), fp64, rounded once
-    float clip = 1.0f;
-    if (F.max_grad_norm > 0.0 && __builtin_isfinite(total)) {
-      const double c = F.max_grad_norm / (__builtin_sqrt(total) + 1e-6);
-      clip = static_cast<float>(c < 1.0 ? c : 1.0);
-    }
-    st->clip_coef = clip;
+    st->clip_coef = clip_multiplier(F.max_grad_norm, total);
   }
 }
 
@@ -452,18 +472,18 @@ __global__ void commit_kernel(const CommitArgs C) {
     st->good_steps = 0;
     return;
   }
-  st->step = st->step + 1;
-  for (int g = 0; g < C.n_groups; ++g) {
-    st->beta1_pow[g] = st->beta1_pow[g] * C.beta1[g];
-    st->beta2_pow[g] = st->beta2_pow[g] * C.beta2[g];
-  }
-  if (C.dynamic) {
-    st->good_steps = st->good_steps + 1;
-    if (C.growth_interval > 0 && st->good_steps == C.growth_interval) {
-      st->loss_scale = static_cast<float>(static_cast<double>(st->loss_scale) * C.growth);
-      st->good_steps = 0;
-    }
-  }
+  advance(st, C.n_groups, C.beta1, C.beta2, C.dynamic != 0, C.growth_interval, C.growth);
+}
+
+// After the second pass of a clipped optimistic step: the other set now holds
+// the clipped update; make it current and count the step.
+__global__ void redo_commit_kernel(const CommitArgs C) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  zero_step_state* st = C.state;
+  if (!st->redo) return;
+  st->redo = 0;
+  st->cur = st->cur ^ 1;
+  advance(st, C.n_groups, C.beta1, C.beta2, true, C.growth_interval, C.growth);
 }
 
 __global__ void state_init_kernel(zero_step_state* st, float loss_scale) {
@@ -481,7 +501,7 @@ __global__ void state_init_kernel(zero_step_state* st, float loss_scale) {
   st->good_steps = 0;
   st->clip_coef = 1.0f;
   st->cur = 0;
-  st->reserved = 0;
+  st->redo = 0;
 }
 
 // ------------------------------------------------------------------------
@@ -542,7 +562,9 @@ __global__ void __launch_bounds__(kBlock) restore_kernel(const RestoreArgs R) {
 
 template <int SRC, bool VEC, int MODE>
 hipError_t adam_launch(const AdamArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((adam_kernel<SRC, VEC, MODE>), dim3(stream_grid(a.n)), dim3(kBlock), 0, s, a);
+  int grid = stream_grid(a.n);
+  if (MODE == kRedo && grid > kRedoGrid) grid = kRedoGrid;
+  hipLaunchKernelGGL((adam_kernel<SRC, VEC, MODE>), dim3(grid), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
@@ -560,6 +582,7 @@ hipError_t launch_adam(const AdamArgs& a, int src, bool vec, int mode, hipStream
     case kFused: return adam_launch<SRC, VEC, kFused>(a, s);                  \
     case kChecked: return adam_launch<SRC, VEC, kChecked>(a, s);              \
     case kOptimistic: return adam_launch<SRC, VEC, kOptimistic>(a, s);        \
+    case kRedo: return adam_launch<SRC, VEC, kRedo>(a, s);                    \
     default: return hipErrorInvalidValue;                                     \
   }
 #define ZDP_ADAM(SRC)                                                         \
@@ -603,6 +626,11 @@ hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s) {
 
 hipError_t launch_commit(const CommitArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(commit_kernel, dim3(1), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_redo_commit(const CommitArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(redo_commit_kernel, dim3(1), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -81,10 +81,11 @@ struct FinalizeArgs {
   zero_step_state* state;
   int32_t n_groups;
   int32_t mode;  // 0: norm, skip verdict, clip multiplier; 1: norm, then commit a static-scale step;
-                 // 2: norm, then commit or discard an optimistic step (dynamic scale)
+                 // 2: norm, then commit or discard an optimistic step (dynamic scale), or, when
+                 //    max_grad_norm asks for clipping, defer the commit to the second pass
   int32_t skip_on_overflow;
   int32_t growth_interval;  // mode 2
-  double max_grad_norm;     // mode 0: clip threshold (0 = none)
+  double max_grad_norm;     // modes 0 and 2: clip threshold (0 = none)
   double backoff, growth, min_scale;  // mode 2
   double beta1[ZERO_MAX_GROUPS];
   double beta2[ZERO_MAX_GROUPS];
@@ -121,7 +122,10 @@ struct RestoreArgs {
 };
 
 enum SrcKind { kSrcAvg = 0, kSrcF16 = 1, kSrcBF16 = 2 };
-enum StepMode { kFused = 0, kChecked = 1, kOptimistic = 2 };
+// kRedo: the second pass of a clipped optimistic step (runs only when the
+// norm asked for clipping; small resident grid so that it costs little otherwise)
+enum StepMode { kFused = 0, kChecked = 1, kOptimistic = 2, kRedo = 3 };
+constexpr int kRedoGrid = 65536;
 
 // Blocks of a streaming launch over n elements.
 inline int stream_grid(int64_t n) {
@@ -137,6 +141,7 @@ hipError_t launch_reduce(const ReduceArgs& a, int src_kind, bool vec, hipStream_
 hipError_t launch_fold(const FoldArgs& a, hipStream_t s);
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
 hipError_t launch_commit(const CommitArgs& a, hipStream_t s);
+hipError_t launch_redo_commit(const CommitArgs& a, hipStream_t s);
 hipError_t launch_state_init(zero_step_state* st, float loss_scale, hipStream_t s);
 hipError_t launch_cast(const CastArgs& a, bool vec, hipStream_t s);
 hipError_t launch_restore(const RestoreArgs& a, bool vec, hipStream_t s);
