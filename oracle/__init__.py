@@ -118,6 +118,9 @@ def lib():
         L.oracle_step.argtypes = [ctypes.POINTER(_Group), ctypes.c_int32,
                                   ctypes.POINTER(_Policy), ctypes.POINTER(_State)]
         L.oracle_step.restype = ctypes.c_int
+        L.oracle_step_given_norm.argtypes = [ctypes.POINTER(_Group), ctypes.c_int32, ctypes.POINTER(_Policy),
+                                             ctypes.POINTER(_State), ctypes.c_double, ctypes.c_int32]
+        L.oracle_step_given_norm.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -289,8 +292,11 @@ class Group:
     _keep: list = field(default_factory=list, repr=False)
 
 
-def step(groups, policy, state):
-    """Run one full step over ``groups`` in place; updates ``state``."""
+def step(groups, policy, state, norm2=None, flag=None):
+    """Run one full step over ``groups`` in place; updates ``state``. With
+    ``norm2`` and ``flag`` given, the groups hold a sample of a shard's
+    coordinates and these are the whole shard's norm² and overflow flag, which
+    the skip verdict and the clip multiplier then use."""
     G = (_Group * len(groups))()
     keep = []
     for i, g in enumerate(groups):
@@ -324,7 +330,13 @@ def step(groups, policy, state):
                 policy.backoff, policy.growth, policy.min_scale, policy.max_grad_norm)
     S = _State(state.step, state.norm2, state.loss_scale, state.overflow,
                state.skipped, state.good_steps, state.clip, 0)
-    rc = lib().oracle_step(G, len(groups), ctypes.byref(P), ctypes.byref(S))
+    if (norm2 is None) != (flag is None):
+        raise ValueError("give both norm2 and flag, or neither")
+    if norm2 is None:
+        rc = lib().oracle_step(G, len(groups), ctypes.byref(P), ctypes.byref(S))
+    else:
+        rc = lib().oracle_step_given_norm(G, len(groups), ctypes.byref(P), ctypes.byref(S),
+                                          ctypes.c_double(norm2), ctypes.c_int32(int(bool(flag))))
     if rc != 0:
         raise RuntimeError(f"oracle_step rc={rc}")
     state.step, state.norm2, state.loss_scale = S.step, S.norm2, S.loss_scale

@@ -386,8 +386,13 @@ static float clip_multiplier(double norm2, double max_norm)
     return (float)(c < 1.0 ? c : 1.0);
 }
 
-int oracle_step(const oracle_group *groups, int32_t n_groups,
-                const oracle_policy *policy, oracle_state *st)
+/* The step of DS12 §6 over `groups`. The overflow flag and the norm come from
+ * these groups' averaged gradients, or, when `given` is set, are the caller's
+ * (given_norm2, given_flag): the flag and norm² of a whole shard of which the
+ * groups hold a sample of coordinates. Everything else is the same. */
+static int step_core(const oracle_group *groups, int32_t n_groups,
+                     const oracle_policy *policy, oracle_state *st,
+                     int given, double given_norm2, int32_t given_flag)
 {
     if (!groups || n_groups < 1 || !policy || !st)
         return OR_EINVAL;
@@ -409,6 +414,10 @@ int oracle_step(const oracle_group *groups, int32_t n_groups,
         oracle_norm_overflow(avg[g], groups[g].n, inv_scale, &norm2, &flag);
     }
     if (rc == OR_OK) {
+        if (given) {
+            norm2 = given_norm2;
+            flag = given_flag;
+        }
         st->norm2 = norm2;
         st->overflow = flag;
         st->clip = clip_multiplier(norm2, policy->max_grad_norm);
@@ -443,4 +452,17 @@ int oracle_step(const oracle_group *groups, int32_t n_groups,
         free(avg[g]);
     free(avg);
     return rc;
+}
+
+int oracle_step(const oracle_group *groups, int32_t n_groups,
+                const oracle_policy *policy, oracle_state *st)
+{
+    return step_core(groups, n_groups, policy, st, 0, 0.0, 0);
+}
+
+int oracle_step_given_norm(const oracle_group *groups, int32_t n_groups,
+                           const oracle_policy *policy, oracle_state *st,
+                           double norm2, int32_t flag)
+{
+    return step_core(groups, n_groups, policy, st, 1, norm2, flag != 0);
 }

@@ -80,10 +80,11 @@ class Run:
     arena over HBM's regions, gradient copies as a pointer table) and the
     oracle's copy of the sampled coordinates."""
 
-    def __init__(self, key, full=False, optimistic=False):
+    def __init__(self, key, full=False, optimistic=False, max_grad_norm=0.0):
         self.wl = wl = WORKLOADS[key]
         self.full = full
         self.optimistic = optimistic
+        self.max_grad_norm = max_grad_norm
         gdt, pdt = torch_dtype(wl.grad_dt), torch_dtype(wl.param_dt)
         self.odt = ORACLE_DT[wl.grad_dt]
         self.groups, self.ogroups, self.samples, self.outside = [], [], [], []
@@ -94,7 +95,8 @@ class Run:
             o_off, o_size, _ = oracle.partition(psi, wl.n_d)
             assert segs[wl.rank] == (int(o_off[wl.rank]), int(o_size[wl.rank]))
             shards.append((psi, *segs[wl.rank]))
-        pipeline = ("optimistic" if optimistic else "checked") if wl.dynamic_loss_scale else "fused"
+        pipeline = ("optimistic" if optimistic else "checked") if wl.dynamic_loss_scale or max_grad_norm > 0 \
+            else "fused"
         specs = layout.step_specs(shards, wl.n_d, gdt, pdt, pipeline, wl.n_d <= layout.INLINE_COPIES)
         buf, self.placement = layout.allocate(specs, DEV, "regions")
         print(f"  layout: {self.placement}", flush=True)
@@ -129,8 +131,9 @@ class Run:
         self.ws = zdp.new_workspace(len(self.groups))
         self.state = zdp.new_state(wl.loss_scale)
         self.ostate = oracle.State(loss_scale=wl.loss_scale)
-        self.policy = oracle.Policy(skip_on_overflow=wl.dynamic_loss_scale)
-        self.policy_ = zdp.policy(True, optimistic=optimistic) if wl.dynamic_loss_scale else None
+        self.policy = oracle.Policy(skip_on_overflow=wl.dynamic_loss_scale, max_grad_norm=max_grad_norm)
+        self.policy_ = (zdp.policy(wl.dynamic_loss_scale, optimistic=optimistic, max_grad_norm=max_grad_norm)
+                        if wl.dynamic_loss_scale or max_grad_norm > 0 else None)
         self.avg = ([buf[(gi, "avg")][:g.master.numel()] for gi, g in enumerate(self.groups)]
                     if pipeline == "checked" else None)
 
@@ -170,7 +173,8 @@ class Run:
         steps = wl.steps if steps is None else steps
         for call in range(1, steps + 1):
             injected = self.draw_grads(call)
-            want_full = call in full_scan_calls or injected
+            # clipping depends on the whole shard's norm: scan it on every call
+            want_full = call in full_scan_calls or injected or self.max_grad_norm > 0
             if want_full:
                 inv = oracle.inv_scale_of(self.ostate.loss_scale)
                 full_n2, full_flag = full_norm_flag([g.replicas for g in self.groups], wl.grad_dt, inv)
@@ -179,7 +183,11 @@ class Run:
                 tidx = torch.from_numpy(idx).to(DEV)
                 og.replicas = [_u16(r[tidx]) for r in g.replicas]
             self.gpu_step()
-            oracle.step(self.ogroups, self.policy, self.ostate)
+            if self.max_grad_norm > 0:
+                # the sampled coordinates stepped with the whole shard's norm and flag
+                oracle.step(self.ogroups, self.policy, self.ostate, norm2=full_n2, flag=full_flag)
+            else:
+                oracle.step(self.ogroups, self.policy, self.ostate)
             torch.cuda.synchronize()
             s = zdp.read_state(self.state)
             tag = f"{wl.key} call {call}"
@@ -187,6 +195,8 @@ class Run:
             assert s["skipped"] == self.ostate.skipped, tag
             assert s["overflow"] == self.ostate.overflow, tag
             assert s["loss_scale"] == np.float32(self.ostate.loss_scale), tag
+            assert s["clip_coef"] == np.float32(self.ostate.clip), (tag, s["clip_coef"], self.ostate.clip)
+            assert s["redo"] == 0, tag
             if want_full:
                 assert s["overflow"] == full_flag, tag
                 if np.isfinite(full_n2):
@@ -251,6 +261,20 @@ def test_13b_nd8_overflow_skip(pipeline):
     st = Run("13b_nd8", optimistic=pipeline == "optimistic").run(full_scan_calls=(1,))
     # ten calls, the fourth overflows: nine applied steps, scale halved once
     assert st.step == 9 and st.loss_scale == 32768.0
+    _free()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("pipeline", ["checked", "optimistic"])
+def test_13b_nd8_clipping(pipeline):
+    # clipping at full size (the norm is about 14, the threshold 10: every applied call clips),
+    # five calls with the overflow on the fourth; the optimistic pipeline's second pass loops over
+    # the shard's 396,729 tiles with its capped grid
+    print(f"[workload] 13b_nd8 clipping ({pipeline})", flush=True)
+    run = Run("13b_nd8", optimistic=pipeline == "optimistic", max_grad_norm=10.0)
+    st = run.run(steps=5)
+    assert st.step == 4 and st.loss_scale == 32768.0 and st.clip < 1.0
+    del run
     _free()
 
 

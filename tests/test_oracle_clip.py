@@ -83,3 +83,33 @@ def test_clip_ignored_on_overflow_and_in_skip():
     st = oracle.State()
     oracle.step([g], oracle.Policy(skip_on_overflow=True, max_grad_norm=0.01), st)
     assert st.skipped == 1 and st.clip == 1.0
+
+
+@pytest.mark.parametrize("max_norm", [0.0, 0.01, 1e6])
+def test_sampled_step_with_the_shard_norm_equals_the_full_step(max_norm):
+    # stepping a sample of coordinates with the whole shard's norm² and flag
+    # (oracle_step_given_norm) gives exactly the full step's values there, over
+    # calls with clipping, an overflow (skip) and scale growth, two groups
+    pol = oracle.Policy(skip_on_overflow=True, growth_interval=2, max_grad_norm=max_norm)
+    full = [_group(6000, 3, 31, wd=0.1, scale=64.0), _group(1500, 3, 32, scale=64.0)]
+    idx = [np.array([0, 1, 2999, 5998, 5999]), np.array([0, 750, 1499])]
+    smp = [oracle.Group(replicas=None, grad_dt=g.grad_dt, master=g.master[i].copy(), m=g.m[i].copy(),
+                        v=g.v[i].copy(), param=None, weight_decay=g.weight_decay) for g, i in zip(full, idx)]
+    sf, ss = oracle.State(loss_scale=64.0), oracle.State(loss_scale=64.0)
+    for k in range(5):
+        for gi, (g, s, i) in enumerate(zip(full, smp, idx)):
+            g.replicas = [grads16_np(g.master.size, "bf16", sf.loss_scale, (33, k, gi, r)) for r in range(3)]
+            if k == 2 and gi == 1:
+                g.replicas[0] = g.replicas[0].copy()
+                g.replicas[0][100] = 0x7F80         # outside the sample: only the shard flag sees it
+            s.replicas = [r[i].copy() for r in g.replicas]
+        oracle.step(full, pol, sf)
+        oracle.step(smp, pol, ss, norm2=sf.norm2, flag=sf.overflow)
+        assert (ss.step, ss.skipped, ss.loss_scale, ss.good_steps, ss.clip) == \
+               (sf.step, sf.skipped, sf.loss_scale, sf.good_steps, sf.clip)
+        for g, s, i in zip(full, smp, idx):
+            for a, b in ((g.master[i], s.master), (g.m[i], s.m), (g.v[i], s.v)):
+                np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert sf.skipped == 0 and sf.step == 4
+    if max_norm == 0.01:
+        assert sf.clip < 1.0
