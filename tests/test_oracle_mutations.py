@@ -56,6 +56,8 @@ MUTATIONS = [
     ("clip multiplier not applied", "g = g * clip;                            /* clip (1 = none) */", "(void)clip;"),
     ("clip from the squared norm", "double c = max_norm / (sqrt(norm2) + 1e-6);", "double c = max_norm / (norm2 + 1e-6);"),
     ("clip allowed to scale up", "return (float)(c < 1.0 ? c : 1.0);", "return (float)c;"),
+    ("shard norm ignored for a sample", "            norm2 = given_norm2;\n", ""),
+    ("shard flag ignored for a sample", "            flag = given_flag;\n", ""),
 ]
 
 
