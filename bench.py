@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--pipeline", choices=["checked", "optimistic"], default="checked",
                    help="dynamic-loss-scale workloads: verdict before the update (checked) or an "
                         "update into a second state set committed afterwards (optimistic)")
+    p.add_argument("--max-grad-norm", type=float, default=0.0,
+                   help="clip the gradient to this global norm (0: off); selects the checked pipeline, or "
+                        "with --pipeline optimistic on a dynamic-scale workload the optimistic one")
     p.add_argument("--arena", choices=["whole", "sized"], default="whole",
                    help="regions placement: the arena is all free memory but 4 GiB (whole) or ends "
                         "at the last planned buffer (sized)")
@@ -88,7 +91,7 @@ class Setup:
     buffers spread over its 96 GiB regions; the default) or "packed" (one
     allocation per buffer)."""
 
-    def __init__(self, wl, dev, optimistic=False, placement="regions", whole=True):
+    def __init__(self, wl, dev, optimistic=False, placement="regions", whole=True, max_grad_norm=0.0):
         import zero_dp_partitioned_amd as zdp
         from zero_dp_partitioned_amd import layout
         from workloads import derive_seed, fill_normal_, torch_dtype
@@ -97,15 +100,19 @@ class Setup:
         self.groups = []
         self.shard = 0
         self.optimistic = optimistic and wl.dynamic_loss_scale
-        pipeline = ("optimistic" if self.optimistic else "checked") if wl.dynamic_loss_scale else "fused"
+        needs_norm = wl.dynamic_loss_scale or max_grad_norm > 0
+        pipeline = ("optimistic" if self.optimistic else "checked") if needs_norm else "fused"
+        self.pipeline = pipeline
         shards = []
         for spec in wl.groups:
             psi = sum(spec.numels)
             segs, _ = zdp.partition(psi, wl.n_d)
             shards.append((psi, *segs[wl.rank]))
         table = placement == "regions" and wl.n_d <= layout.INLINE_COPIES
+        # with one copy the checked pipeline scans it instead of writing an average
+        spec_pipeline = "fused" if pipeline == "checked" and wl.n_d == 1 else pipeline
         specs = layout.step_specs(shards, wl.n_d, torch_dtype(wl.grad_dt), torch_dtype(wl.param_dt),
-                                  pipeline, table)
+                                  spec_pipeline, table)
         buf, self.placement = layout.allocate(specs, dev, placement, whole=whole)
         for gi, (spec, (psi, off, n)) in enumerate(zip(wl.groups, shards)):
             master = buf[(gi, "master")][:n]
@@ -127,8 +134,9 @@ class Setup:
             self.shard += n
         self.ws = zdp.new_workspace(len(self.groups))
         self.state = zdp.new_state(wl.loss_scale)
-        self.policy = zdp.policy(True, optimistic=self.optimistic) if wl.dynamic_loss_scale else None
-        if pipeline == "checked":
+        self.policy = (zdp.policy(wl.dynamic_loss_scale, optimistic=self.optimistic, max_grad_norm=max_grad_norm)
+                       if needs_norm else None)
+        if spec_pipeline == "checked":
             self.avg = [buf[(gi, "avg")][:g.master.numel()] for gi, g in enumerate(self.groups)]
 
     def step(self):
@@ -136,7 +144,13 @@ class Setup:
         if self.policy is None or self.optimistic:
             zdp.adam_step(self.groups, self.ws, self.state, self.policy)
             return
-        # dynamic loss scale: average pass, norm / overflow verdict, checked update
+        # checked pipeline (dynamic scale or clipping): norm / overflow verdict, then the update
+        if self.wl.n_d == 1:
+            # a single copy: scan it for the norm, then the update reads it again
+            zdp.grad_norm_overflow([g.replicas[0] for g in self.groups], self.ws, len(self.groups), self.state,
+                                   self.policy)
+            zdp.adam_step(self.groups, self.ws, self.state, self.policy)
+            return
         for gi, g in enumerate(self.groups):
             zdp.reduce_grad_segment(g.replicas, self.avg[gi], self.ws, gi, self.state)
         zdp.grad_norm_overflow(None, self.ws, len(self.groups), self.state, self.policy)
@@ -232,7 +246,7 @@ def main():
     wl = WORKLOADS[args.workload]
     log(args, f"workload {wl.key}: {wl.title}")
     setup = Setup(wl, dev, optimistic=args.pipeline == "optimistic", placement=args.placement,
-                  whole=args.arena == "whole")
+                  whole=args.arena == "whole", max_grad_norm=args.max_grad_norm)
     S = setup.shard
     bpp = bytes_per_param(wl.n_d)
     log(args, f"shard {S} params, {len(setup.groups)} group(s), {bpp} B/param, "
@@ -261,7 +275,7 @@ def main():
     value = S / (ms_per_step / 1e3)
     algo_bytes = S * bpp
     achieved = algo_bytes / (ev_mean / 1e3) / 1e9
-    pipeline = ("optimistic" if setup.optimistic else "checked") if wl.dynamic_loss_scale else "fused"
+    pipeline = setup.pipeline
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         key = wl.key if pipeline == "fused" else f"{wl.key}:{pipeline}"
@@ -287,7 +301,7 @@ def main():
         "config": {"workload": wl.key, "shard_params": S, "n_d": wl.n_d, "rank": wl.rank,
                    "groups": len(setup.groups), "grad_dtype": wl.grad_dt, "param_dtype": wl.param_dt,
                    "loss_scale": wl.loss_scale, "dynamic_loss_scale": wl.dynamic_loss_scale,
-                   "pipeline": pipeline,
+                   "pipeline": pipeline, "max_grad_norm": args.max_grad_norm,
                    "bytes_per_param": bpp, **setup.placement},
         "gbps": achieved,
         "pct_peak": 100.0 * achieved / PEAK_HBM_GBPS,
