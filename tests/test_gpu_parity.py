@@ -209,9 +209,12 @@ def test_checked_pipeline_skip_and_scale(n, n_d, dt, use_avg):
     assert_u16_equal(down16(flat)[off:off + n], og.param, tag + " param")
 
 
-def test_checked_single_copy_prepass_two_groups():
+@pytest.mark.parametrize("mis", [0, 1, 4])
+def test_checked_single_copy_prepass_two_groups(mis):
     """N_d = 1, two groups, dynamic scale: the norm pass scans the gradients
-    directly, then the update re-reads them."""
+    directly, then the update re-reads them. mis: the copies start that many
+    elements into their buffers (0: 16-byte aligned, the wide-load scan; 4:
+    8-byte, 1: 2-byte aligned, the streaming pass's quad and element paths)."""
     dt = "bf16"
     odt = ORACLE_DT[dt]
     sizes, wds = (30_011, 513), (0.1, 0.0)
@@ -233,7 +236,7 @@ def test_checked_single_copy_prepass_two_groups():
         if k == 1:
             grads[1] = grads[1].copy()
             grads[1][0] = 0xFF80   # -inf in the small group voids the whole step
-        dg = [up16(g, dt) for g in grads]
+        dg = [carve(g.size + 8, mis, g.size, TORCH16[dt]).copy_(up16(g, dt)) for g in grads]
         zdp.grad_norm_overflow(dg, ws, 2, st, sc)
         for G, d in zip(dev_groups, dg):
             G.replicas = [d]

@@ -97,7 +97,8 @@ class Run:
             shards.append((psi, *segs[wl.rank]))
         pipeline = ("optimistic" if optimistic else "checked") if wl.dynamic_loss_scale or max_grad_norm > 0 \
             else "fused"
-        specs = layout.step_specs(shards, wl.n_d, gdt, pdt, pipeline, wl.n_d <= layout.INLINE_COPIES)
+        spec_pipeline = "fused" if pipeline == "checked" and wl.n_d == 1 else pipeline
+        specs = layout.step_specs(shards, wl.n_d, gdt, pdt, spec_pipeline, wl.n_d <= layout.INLINE_COPIES)
         buf, self.placement = layout.allocate(specs, DEV, "regions")
         print(f"  layout: {self.placement}", flush=True)
         for gi, (spec, (psi, off, n)) in enumerate(zip(wl.groups, shards)):
@@ -135,7 +136,7 @@ class Run:
         self.policy_ = (zdp.policy(wl.dynamic_loss_scale, optimistic=optimistic, max_grad_norm=max_grad_norm)
                         if wl.dynamic_loss_scale or max_grad_norm > 0 else None)
         self.avg = ([buf[(gi, "avg")][:g.master.numel()] for gi, g in enumerate(self.groups)]
-                    if pipeline == "checked" else None)
+                    if spec_pipeline == "checked" else None)
 
     def draw_grads(self, call):
         wl = self.wl
@@ -154,6 +155,12 @@ class Run:
 
     def gpu_step(self):
         if self.policy_ is None or self.optimistic:
+            zdp.adam_step(self.groups, self.ws, self.state, self.policy_)
+            return
+        if self.wl.n_d == 1:
+            # checked pipeline with a single copy: scan it, then the update reads it again (as bench.py)
+            zdp.grad_norm_overflow([g.replicas[0] for g in self.groups], self.ws, len(self.groups), self.state,
+                                   self.policy_)
             zdp.adam_step(self.groups, self.ws, self.state, self.policy_)
             return
         for gi, g in enumerate(self.groups):
@@ -261,6 +268,18 @@ def test_13b_nd8_overflow_skip(pipeline):
     st = Run("13b_nd8", optimistic=pipeline == "optimistic").run(full_scan_calls=(1,))
     # ten calls, the fourth overflows: nine applied steps, scale halved once
     assert st.step == 9 and st.loss_scale == 32768.0
+    _free()
+
+
+@pytest.mark.timeout(900)
+def test_gpt2_1_5b_clipping():
+    # clipping on the single-copy shard (the norm is about 39, the threshold 1): the checked pipeline
+    # scans the copy first (the wide-load scan loops its capped grid over 380,277 tiles), then updates
+    print("[workload] gpt2_1.5b clipping", flush=True)
+    run = Run("gpt2_1.5b", max_grad_norm=1.0)
+    st = run.run(steps=3)
+    assert st.step == 3 and st.clip < 1.0
+    del run
     _free()
 
 

@@ -65,12 +65,12 @@ int check_device() {
 double* level2_of(void* ws, int32_t g) { return static_cast<double*>(ws) + static_cast<int64_t>(g) * kFoldBlocks; }
 double* scratch_of(void* ws) { return reinterpret_cast<double*>(static_cast<char*>(ws) + kHeaderBytes); }
 
-// Reduce the block partials a streaming launch over n elements just wrote
-// into the level-2 partials of group g.
-hipError_t fold_into(void* ws, int32_t g, int64_t n, hipStream_t s) {
+// Reduce the `blocks` partials a launch just wrote into the level-2 partials
+// of group g (a streaming launch over n elements has stream_grid(n) blocks).
+hipError_t fold_into(void* ws, int32_t g, int64_t blocks, hipStream_t s) {
   FoldArgs F;
   F.partials = scratch_of(ws);
-  F.count = stream_grid(n);
+  F.count = blocks;
   F.level2 = level2_of(ws, g);
   return launch_fold(F, s);
 }
@@ -318,7 +318,7 @@ int zero_reduce_grad_segment(const void* const* replicas, int32_t n_d, int32_t g
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = launch_reduce(R, grad_dt == ZERO_DT_BF16 ? kSrcBF16 : kSrcF16, vec, s);
   if (e != hipSuccess) return hip_fail(e, "reduce launch");
-  e = fold_into(workspace, group, n, s);
+  e = fold_into(workspace, group, stream_grid(n), s);
   return e == hipSuccess ? ZERO_OK : hip_fail(e, "fold launch");
 }
 
@@ -353,9 +353,11 @@ int zero_grad_norm_overflow(const void* const* grads, const int64_t* counts, int
   const int src = grad_dt == ZERO_DT_BF16 ? kSrcBF16 : kSrcF16;
   for (int32_t g = 0; g < n_groups; ++g) {
     if (!scan[g]) continue;
-    hipError_t e = launch_reduce(R[g], src, vec[g], s);
+    // 16-byte-aligned copies take the wide-load scan; others the streaming pass
+    const bool wide = aligned(grads[g], 16);
+    hipError_t e = wide ? launch_scan(R[g], src, s) : launch_reduce(R[g], src, vec[g], s);
     if (e != hipSuccess) return hip_fail(e, "scan launch");
-    e = fold_into(workspace, g, R[g].n, s);
+    e = fold_into(workspace, g, wide ? scan_grid(R[g].n) : stream_grid(R[g].n), s);
     if (e != hipSuccess) return hip_fail(e, "fold launch");
   }
   FinalizeArgs F;
@@ -458,7 +460,7 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_policy
     hipError_t e = launch_adam(A[g], src[g], vec[g], mode, s);
     if (e != hipSuccess) return hip_fail(e, "update launch");
     if (!checked) {
-      e = fold_into(workspace, g, A[g].n, s);
+      e = fold_into(workspace, g, stream_grid(A[g].n), s);
       if (e != hipSuccess) return hip_fail(e, "fold launch");
     }
   }

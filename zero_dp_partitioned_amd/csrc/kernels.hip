@@ -32,6 +32,7 @@ namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef unsigned u2 __attribute__((ext_vector_type(2)));
+typedef unsigned u4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------------
 // Streaming accesses. Every byte a step touches is read once and written
@@ -363,6 +364,45 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(const ReduceArgs R) {
 }
 
 // ------------------------------------------------------------------------
+// Scan of one 16-byte-aligned gradient copy (N_d = 1, no average written):
+// the norm / overflow partials only. Lanes take 8 consecutive elements
+// (16-byte loads), tiles of 4096 as elsewhere; a capped grid loops over the
+// tiles, so each block reads many tiles and its fixed costs amortise.
+// ------------------------------------------------------------------------
+
+template <int SRC>
+__global__ void __launch_bounds__(kBlock) scan_kernel(const ReduceArgs R) {
+  const float inv_scale = static_cast<float>(1.0 / static_cast<double>(R.state->loss_scale));
+  const uint16_t* const src = static_cast<const uint16_t*>(R.src.rep[0]);
+  double sumsq = 0.0;
+  int bad = 0;
+  const int64_t n = R.n;
+  const int64_t ntiles = (n + kTile - 1) / kTile;
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+#pragma unroll
+    for (int k = 0; k < kTile / (kBlock * 8); ++k) {
+      const int64_t e = t * kTile + static_cast<int64_t>(k * kBlock + threadIdx.x) * 8;
+      if (e + 8 <= n) {
+        const u4 x = ld_stream(reinterpret_cast<const u4*>(src + e));
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float lo = decode16<SRC>(w[q] & 0xFFFFu), hi = decode16<SRC>(w[q] >> 16);
+          account(lo, lo * inv_scale, sumsq, bad);
+          account(hi, hi * inv_scale, sumsq, bad);
+        }
+      } else {
+        for (int64_t j = e; j < n && j < e + 8; ++j) {
+          const float a = decode16<SRC>(src[j]);
+          account(a, a * inv_scale, sumsq, bad);
+        }
+      }
+    }
+  }
+  write_block_partial(sumsq, bad, R.partials);
+}
+
+// ------------------------------------------------------------------------
 // Fold: block j of kFoldBlocks sums partials [j*C, min((j+1)*C, count)) with
 // C = ceil(count / kFoldBlocks), thread i taking i, i+256, ... of the range.
 // ------------------------------------------------------------------------
@@ -612,6 +652,19 @@ hipError_t launch_reduce(const ReduceArgs& a, int src, bool vec, hipStream_t s) 
   if (src == kSrcF16) return vec ? reduce_launch<kSrcF16, true>(a, s) : reduce_launch<kSrcF16, false>(a, s);
   if (src == kSrcBF16) return vec ? reduce_launch<kSrcBF16, true>(a, s) : reduce_launch<kSrcBF16, false>(a, s);
   return hipErrorInvalidValue;
+}
+
+int scan_grid(int64_t n) {
+  const int g = stream_grid(n);
+  return g < kScanGrid ? g : kScanGrid;
+}
+
+hipError_t launch_scan(const ReduceArgs& a, int src, hipStream_t s) {
+  const dim3 grid(scan_grid(a.n));
+  if (src == kSrcF16) hipLaunchKernelGGL(scan_kernel<kSrcF16>, grid, dim3(kBlock), 0, s, a);
+  else if (src == kSrcBF16) hipLaunchKernelGGL(scan_kernel<kSrcBF16>, grid, dim3(kBlock), 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_fold(const FoldArgs& a, hipStream_t s) {

@@ -126,6 +126,7 @@ enum SrcKind { kSrcAvg = 0, kSrcF16 = 1, kSrcBF16 = 2 };
 // norm asked for clipping; small resident grid so that it costs little otherwise)
 enum StepMode { kFused = 0, kChecked = 1, kOptimistic = 2, kRedo = 3 };
 constexpr int kRedoGrid = 65536;
+constexpr int kScanGrid = 65536;  // blocks of the single-copy scan (each loops over tiles)
 
 // Blocks of a streaming launch over n elements.
 inline int stream_grid(int64_t n) {
@@ -138,6 +139,9 @@ inline int stream_grid(int64_t n) {
 // `vec` selects the aligned quad path.
 hipError_t launch_adam(const AdamArgs& a, int src_kind, bool vec, int mode, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, int src_kind, bool vec, hipStream_t s);
+// Single-copy scan (partials only) of a 16-byte-aligned copy; scan_grid(n) blocks, one partial each.
+hipError_t launch_scan(const ReduceArgs& a, int src_kind, hipStream_t s);
+int scan_grid(int64_t n);
 hipError_t launch_fold(const FoldArgs& a, hipStream_t s);
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
 hipError_t launch_commit(const CommitArgs& a, hipStream_t s);
