@@ -1,6 +1,6 @@
 """Random parity sweep: seeded random configurations of the whole step against
 the oracle, bit for bit, three calls each. Each case draws 1-3 groups (shard
-length 1..40,000, N_d per group from 1-9, 64 or 65, parameter offset and
+length 1..40,000, or 1.5M..6M in the large cases, N_d per group from 1-9, 64 or 65, parameter offset and
 alignment, unaligned fp32 state), a gradient dtype, a copy layout (pointer
 table, equally spaced buffer, packed unaligned), a pipeline (fused, checked,
 optimistic) with or without clipping, a loss scale, and an inf or NaN written
@@ -21,15 +21,21 @@ pytestmark = pytest.mark.gpu
 N_CASES = 200
 
 
-def _case(seed):
-    rng = np.random.Generator(np.random.PCG64(seed))
+N_LARGE = 16
+
+
+def _case(seed, large=False):
+    rng = np.random.Generator(np.random.PCG64(seed + (1 << 20 if large else 0)))
     dt = ["f16", "bf16"][rng.integers(2)]
     pipeline = ["fused", "checked", "optimistic"][rng.integers(3)]
     clip = bool(rng.integers(2)) and pipeline != "fused"
     groups = []
-    for _ in range(int(rng.integers(1, 4))):
-        n = int(rng.choice([1, 7, 8, 9, 255, 4096, 4097, int(rng.integers(1, 40_000))]))
-        n_d = int(rng.choice([1, 1, 2, 3, 4, 5, 8, 9, 64, 65]))
+    for _ in range(int(rng.integers(1, 3 if large else 4))):
+        if large:   # beyond the restore kernel's 1,024-block grid: its blocks loop over tiles
+            n, n_d = int(rng.integers(1_500_000, 6_000_000)), int(rng.choice([1, 2, 4, 8]))
+        else:
+            n = int(rng.choice([1, 7, 8, 9, 255, 4096, 4097, int(rng.integers(1, 40_000))]))
+            n_d = int(rng.choice([1, 1, 2, 3, 4, 5, 8, 9, 64, 65]))
         layout = "strided" if n_d > 64 else ["table", "strided", "packed"][rng.integers(3)]
         groups.append(dict(n=n, n_d=n_d, layout=layout, off=int(rng.integers(0, 9)),
                            mis=int(rng.choice([0, 0, 0, 1, 2])), wd=float(rng.choice([0.0, 0.1]))))
@@ -42,7 +48,16 @@ def _case(seed):
 
 @pytest.mark.parametrize("seed", range(N_CASES))
 def test_random_configuration(seed):
-    dt, pipeline, clip, specs, scale, max_norm, inject = _case(seed)
+    run_case(seed, _case(seed))
+
+
+@pytest.mark.parametrize("seed", range(N_LARGE))
+def test_random_large_configuration(seed):
+    run_case(seed, _case(seed, large=True))
+
+
+def run_case(seed, case):
+    dt, pipeline, clip, specs, scale, max_norm, inject = case
     dynamic = pipeline != "fused" and (pipeline == "optimistic" or seed % 2 == 0)
     tag = f"seed {seed}: {dt} {pipeline} dynamic={dynamic} clip={max_norm:.3g} scale={scale} groups={specs}"
     print(f"[case] {tag}", flush=True)
