@@ -36,7 +36,14 @@ def bytes_per_param(n_d):
 
 
 def kernel_source_hash():
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the kernel source's code: comments and whitespace are removed
+    first, so that only a change to the code invalidates recorded counters."""
+    import re
+    src = open(KERNEL_SRC).read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    src = " ".join(src.split())
+    return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
 def parse():

@@ -20,6 +20,11 @@
 // kernel reduces a launch's partials into 256 per-group values, and a one-block
 // kernel combines those. Every reduction has a fixed shape, so the norm is the
 // same bit pattern run after run.
+//
+// The exceptions to one block per tile are launches that either rarely do any
+// work or are bound by per-block costs: the restore and second-pass launches
+// of the optimistic pipeline (they exit at once unless a step was voided or
+// clipped) and the single-copy scan (16-byte loads, a block reads many tiles).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -238,6 +243,8 @@ __device__ __forceinline__ void write_block_partial(double s, int bad, double* o
 //   kChecked: exits if the step was voided; clip multiplier; no partials.
 //   kOptimistic: as kFused, but reads the current state set and writes the
 //     other one (state->cur picks which is which).
+//   kRedo: the second pass of a clipped optimistic step: exits unless
+//     state->redo; as kOptimistic with the clip multiplier, no partials.
 // VEC: fp32 arrays 16-byte and 16-bit copies 8-byte aligned (quad path).
 // ------------------------------------------------------------------------
 
