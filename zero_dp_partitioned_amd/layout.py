@@ -75,9 +75,10 @@ def allocate(specs, device, placement="regions", reserve_bytes=4 << 30, whole=Tr
     HBM in address order, so the planned offsets fall into the physical
     regions. A smaller arena (whole=False: up to the end of the last buffer)
     is backed wherever the driver finds room, which can put every planned
-    region into one physical one. The space after the planned buffers stays
-    free for the caller's other data. A step under SMALL_STEP_BYTES gets a
-    small arena in one region."""
+    region into one physical one; it is also what `whole` falls back to if
+    the whole-memory allocation fails (info["arena"] then says so). The space
+    after the planned buffers stays free for the caller's other data. A step
+    under SMALL_STEP_BYTES gets a small arena in one region."""
     import torch
     if placement not in PLACEMENTS:
         raise ValueError(f"unknown placement {placement!r}")
@@ -90,9 +91,16 @@ def allocate(specs, device, placement="regions", reserve_bytes=4 << 30, whole=Tr
         n_regions = 1 if sum(sizes) < SMALL_STEP_BYTES else 0
         offs, regs, total = plan_arena(sizes, [s.traffic for s in specs], free - reserve_bytes,
                                        n_regions=n_regions)
+        arena = None
         if whole and n_regions != 1:
-            total = (free - reserve_bytes) // ARENA_ALIGN * ARENA_ALIGN
-        arena = torch.empty(total, dtype=torch.uint8, device=device)
+            try:
+                arena = torch.empty((free - reserve_bytes) // ARENA_ALIGN * ARENA_ALIGN, dtype=torch.uint8,
+                                    device=device)
+                total = arena.numel()
+            except torch.cuda.OutOfMemoryError:
+                info["arena"] = "sized: the whole-memory arena could not be allocated"
+        if arena is None:
+            arena = torch.empty(total, dtype=torch.uint8, device=device)
         for s, o in zip(specs, offs):
             bufs[s.key] = arena_view(arena, o, max(1, s.numel), s.dtype)
         info.update(arena_bytes=total, regions=len(set(regs)))
