@@ -150,6 +150,41 @@ __device__ __forceinline__ void source4(const GradSource& S, int64_t e, float a[
   }
 }
 
+// Averaged gradients of a lane's four quads of a full tile (quads at t0 +
+// (k*256 + lane)*4, k = 0..3), copy by copy: each copy's four quads are read
+// together, so a block takes each copy's 8 KiB of the tile in one visit
+// instead of four. The additions per element stay in replica order.
+template <int SRC>
+__device__ __forceinline__ void source16(const GradSource& S, int64_t t0, float a[4][4]) {
+  float acc[4][4] = {};
+  const int nd = S.n_d;
+  const int64_t lane4 = static_cast<int64_t>(threadIdx.x) * 4;
+  int r = 0;
+  for (; r + 8 <= nd; r += 8) {
+    u2 x[8][4];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        x[q][k] = ld_stream(reinterpret_cast<const u2*>(replica(S, r + q) + t0 + k * kBlock * 4 + lane4));
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) accumulate4<SRC>(acc[k], x[q][k]);
+  }
+  for (; r < nd; ++r) {
+    u2 x[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = ld_stream(reinterpret_cast<const u2*>(replica(S, r) + t0 + k * kBlock * 4 + lane4));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) accumulate4<SRC>(acc[k], x[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) a[k][q] = finish_average(acc[k][q], S);
+}
+
 // Averaged gradient of one element (any alignment).
 template <int SRC>
 __device__ __forceinline__ float source1(const GradSource& S, int64_t j) {
@@ -296,35 +331,51 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs A) {
     if (pdt) param[j] = static_cast<uint16_t>(encode16(th, pdt));
   };
 
+  // one quad's update from its averaged gradient a[4] (quad path)
+  auto quad = [&](int64_t e, const float a[4]) {
+    const f4 t4 = ld_stream(reinterpret_cast<const f4*>(mst_in + e));
+    const f4 m4 = ld_stream(reinterpret_cast<const f4*>(m_in + e));
+    const f4 v4 = ld_stream(reinterpret_cast<const f4*>(v_in + e));
+    float th[4] = {t4.x, t4.y, t4.z, t4.w};
+    float mm[4] = {m4.x, m4.y, m4.z, m4.w};
+    float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float g = a[q] * s.inv_scale;
+      if constexpr (!CLIPPED) account(a[q], g, sumsq, bad);
+      if constexpr (CLIPPED) g = g * s.clip;
+      adam1(g, th[q], mm[q], vv[q], s);
+    }
+    st_stream(reinterpret_cast<f4*>(mst_out + e), (f4){th[0], th[1], th[2], th[3]});
+    st_stream(reinterpret_cast<f4*>(m_out + e), (f4){mm[0], mm[1], mm[2], mm[3]});
+    st_stream(reinterpret_cast<f4*>(v_out + e), (f4){vv[0], vv[1], vv[2], vv[3]});
+    if (pdt) {
+      uint32_t h[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) h[q] = encode16(th[q], pdt);
+      store4_16(param + e, h, A.param_align);
+    }
+  };
+
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    if constexpr (VEC && SRC != kSrcAvg) {
+      // several copies, a full tile: read them copy by copy (source16)
+      if (A.src.n_d > 1 && (t + 1) * kTile <= n) {
+        float a16[4][4];
+        source16<SRC>(A.src, t * kTile, a16);
+#pragma unroll
+        for (int k = 0; k < kQuadsPerThread; ++k)
+          quad(t * kTile + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4, a16[k]);
+        continue;
+      }
+    }
 #pragma unroll
     for (int k = 0; k < kQuadsPerThread; ++k) {
       const int64_t e = t * kTile + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4;
       if (VEC && e + 4 <= n) {
         float a[4];
         source4<SRC>(A.src, e, a);
-        const f4 t4 = ld_stream(reinterpret_cast<const f4*>(mst_in + e));
-        const f4 m4 = ld_stream(reinterpret_cast<const f4*>(m_in + e));
-        const f4 v4 = ld_stream(reinterpret_cast<const f4*>(v_in + e));
-        float th[4] = {t4.x, t4.y, t4.z, t4.w};
-        float mm[4] = {m4.x, m4.y, m4.z, m4.w};
-        float vv[4] = {v4.x, v4.y, v4.z, v4.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float g = a[q] * s.inv_scale;
-          if constexpr (!CLIPPED) account(a[q], g, sumsq, bad);
-          if constexpr (CLIPPED) g = g * s.clip;
-          adam1(g, th[q], mm[q], vv[q], s);
-        }
-        st_stream(reinterpret_cast<f4*>(mst_out + e), (f4){th[0], th[1], th[2], th[3]});
-        st_stream(reinterpret_cast<f4*>(m_out + e), (f4){mm[0], mm[1], mm[2], mm[3]});
-        st_stream(reinterpret_cast<f4*>(v_out + e), (f4){vv[0], vv[1], vv[2], vv[3]});
-        if (pdt) {
-          uint32_t h[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) h[q] = encode16(th[q], pdt);
-          store4_16(param + e, h, A.param_align);
-        }
+        quad(e, a);
       } else {
         for (int q = 0; q < 4; ++q)
           if (e + q < n) one(e + q);
@@ -348,6 +399,21 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(const ReduceArgs R) {
   const int64_t n = R.n;
   const int64_t ntiles = (n + kTile - 1) / kTile;
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    if constexpr (VEC) {
+      // several copies, a full tile: read them copy by copy (source16)
+      if (R.src.n_d > 1 && (t + 1) * kTile <= n) {
+        float a16[4][4];
+        source16<SRC>(R.src, t * kTile, a16);
+#pragma unroll
+        for (int k = 0; k < kQuadsPerThread; ++k) {
+          const int64_t e = t * kTile + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) account(a16[k][q], a16[k][q] * inv_scale, sumsq, bad);
+          if (out) st_stream(reinterpret_cast<f4*>(out + e), (f4){a16[k][0], a16[k][1], a16[k][2], a16[k][3]});
+        }
+        continue;
+      }
+    }
 #pragma unroll
     for (int k = 0; k < kQuadsPerThread; ++k) {
       const int64_t e = t * kTile + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4;
