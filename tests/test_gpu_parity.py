@@ -122,6 +122,9 @@ FUSED_CASES = [
     (65_541, 64, "bf16", 12, 0, "strided"),
     (30_001, 65, "f16", 0, 0, "strided"),
     (30_001, 100, "bf16", 2, 0, "strided"),
+    (40_961, 32, "f16", 2, 0, "table"),         # 32+ copies: tiles of 8192, five full + a ragged tail
+    (24_577, 48, "bf16", 0, 0, "table"),        # 48 copies: division by N_d, three wide tiles + tail
+    (8_191, 32, "f16", 1, 0, "strided"),        # under one wide tile: the tail path only
     (50_000, 8, "f16", 0, 0, "packed"),         # unaligned copies: element path
     (50_001, 2, "bf16", 0, 1, "table"),         # unaligned fp32 state: element path
     (4_500_001, 1, "bf16", 0, 0, "table"),      # more than one grid-stride round
@@ -404,7 +407,7 @@ def test_fused_pipeline_reports_no_clip():
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("n,n_d,dt,off,misalign", [(70_001, 8, "f16", 3, 0), (4099, 1, "bf16", 0, 0),
-                                                   (30_000, 2, "f16", 8, 1)])
+                                                   (30_000, 2, "f16", 8, 1), (40_961, 32, "bf16", 5, 0)])
 def test_optimistic_pipeline(n, n_d, dt, off, misalign):
     tag = f"optimistic n={n} n_d={n_d} {dt} off={off} mis={misalign}"
     print(f"[case] {tag}", flush=True)
@@ -553,7 +556,8 @@ def test_fused_step_in_a_planned_arena():
 # norm says to clip; the results are the checked pipeline's (the oracle's)
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("sizes,n_d,dt", [((30_011,), 4, "f16"), ((20_000, 4_099), 2, "bf16"), ((9_001,), 1, "f16")])
+@pytest.mark.parametrize("sizes,n_d,dt", [((30_011,), 4, "f16"), ((20_000, 4_099), 2, "bf16"), ((9_001,), 1, "f16"),
+                                          ((24_577, 9_001), 32, "f16")])
 def test_optimistic_pipeline_with_clipping(sizes, n_d, dt):
     tag = f"optimistic+clip sizes={sizes} n_d={n_d} {dt}"
     print(f"[case] {tag}", flush=True)

@@ -66,7 +66,7 @@ double* level2_of(void* ws, int32_t g) { return static_cast<double*>(ws) + stati
 double* scratch_of(void* ws) { return reinterpret_cast<double*>(static_cast<char*>(ws) + kHeaderBytes); }
 
 // Reduce the `blocks` partials a launch just wrote into the level-2 partials
-// of group g (a streaming launch over n elements has stream_grid(n) blocks).
+// of group g (the launchers report their grid size).
 hipError_t fold_into(void* ws, int32_t g, int64_t blocks, hipStream_t s) {
   FoldArgs F;
   F.partials = scratch_of(ws);
@@ -316,9 +316,10 @@ int zero_reduce_grad_segment(const void* const* replicas, int32_t n_d, int32_t g
   R.state = state;
   R.partials = scratch_of(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_reduce(R, grad_dt == ZERO_DT_BF16 ? kSrcBF16 : kSrcF16, vec, s);
+  int blocks = 0;
+  hipError_t e = launch_reduce(R, grad_dt == ZERO_DT_BF16 ? kSrcBF16 : kSrcF16, vec, s, &blocks);
   if (e != hipSuccess) return hip_fail(e, "reduce launch");
-  e = fold_into(workspace, group, stream_grid(n), s);
+  e = fold_into(workspace, group, blocks, s);
   return e == hipSuccess ? ZERO_OK : hip_fail(e, "fold launch");
 }
 
@@ -355,9 +356,10 @@ int zero_grad_norm_overflow(const void* const* grads, const int64_t* counts, int
     if (!scan[g]) continue;
     // 16-byte-aligned copies take the wide-load scan; others the streaming pass
     const bool wide = aligned(grads[g], 16);
-    hipError_t e = wide ? launch_scan(R[g], src, s) : launch_reduce(R[g], src, vec[g], s);
+    int blocks = scan_grid(R[g].n);
+    hipError_t e = wide ? launch_scan(R[g], src, s) : launch_reduce(R[g], src, vec[g], s, &blocks);
     if (e != hipSuccess) return hip_fail(e, "scan launch");
-    e = fold_into(workspace, g, wide ? scan_grid(R[g].n) : stream_grid(R[g].n), s);
+    e = fold_into(workspace, g, blocks, s);
     if (e != hipSuccess) return hip_fail(e, "fold launch");
   }
   FinalizeArgs F;
@@ -457,10 +459,11 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_policy
   if (int rc = check_device()) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   for (int32_t g = 0; g < n_groups; ++g) {
-    hipError_t e = launch_adam(A[g], src[g], vec[g], mode, s);
+    int blocks = 0;
+    hipError_t e = launch_adam(A[g], src[g], vec[g], mode, s, &blocks);
     if (e != hipSuccess) return hip_fail(e, "update launch");
     if (!checked) {
-      e = fold_into(workspace, g, stream_grid(A[g].n), s);
+      e = fold_into(workspace, g, blocks, s);
       if (e != hipSuccess) return hip_fail(e, "fold launch");
     }
   }
@@ -509,7 +512,8 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_policy
       for (int32_t g = 0; g < n_groups; ++g) {
         AdamArgs a = A[g];
         a.partials = nullptr;
-        e = launch_adam(a, src[g], vec[g], kRedo, s);
+        int blocks = 0;
+        e = launch_adam(a, src[g], vec[g], kRedo, s, &blocks);
         if (e != hipSuccess) return hip_fail(e, "second-pass launch");
       }
       CommitArgs C;

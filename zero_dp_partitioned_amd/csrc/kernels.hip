@@ -8,7 +8,9 @@
 // run. One block per tile: the hardware dispatcher hands out tiles in order,
 // which keeps the resident blocks on one advancing window of HBM; on gfx950
 // this sustains clearly more bandwidth for a read-modify-write stream than a
-// resident grid looping over the vector.
+// resident grid looping over the vector. With 32 or more gradient copies the
+// update kernel's lanes take 8 quads (8192-element tiles) and read the copies
+// one after another with a cap on the loads in flight (source_tile).
 //
 // Numerics follow the per-coordinate Adam update of the ZeRO reading notes
 // (second part, §3) in fp32 with one rounding per operation: fp-contract is off
@@ -150,37 +152,60 @@ __device__ __forceinline__ void source4(const GradSource& S, int64_t e, float a[
   }
 }
 
-// Averaged gradients of a lane's four quads of a full tile (quads at t0 +
-// (k*256 + lane)*4, k = 0..3), copy by copy: each copy's four quads are read
-// together, so a block takes each copy's 8 KiB of the tile in one visit
-// instead of four. The additions per element stay in replica order.
-template <int SRC>
-__device__ __forceinline__ void source16(const GradSource& S, int64_t t0, float a[4][4]) {
-  float acc[4][4] = {};
+// Waits until at most N-1 of the wave's vector loads are outstanding.
+template <int N>
+__device__ __forceinline__ void bound_loads_in_flight() {
+  static_assert(N >= 1 && N <= 8, "bound of 1-8 loads");
+  if constexpr (N == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+  else if constexpr (N == 3) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+  else if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+  else if constexpr (N == 7) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
+}
+
+// Averaged gradients of a lane's QL quads of a full tile (quads at t0 +
+// (k*256 + lane)*4, k < QL), copy by copy: a block reads copy 0's QL * 2 KiB
+// of the tile, then copy 1's, and so on. INFL > 0 caps the gradient loads a
+// wave has in flight at INFL; INFL = 0 issues eight copies' loads at once.
+// With many copies the capped order is faster: the requests HBM has queued
+// then fall into few DRAM rows at a time. The additions per element stay in
+// replica order either way.
+template <int SRC, int QL, int INFL>
+__device__ __forceinline__ void source_tile(const GradSource& S, int64_t t0, float a[QL][4]) {
+  float acc[QL][4] = {};
   const int nd = S.n_d;
   const int64_t lane4 = static_cast<int64_t>(threadIdx.x) * 4;
   int r = 0;
-  for (; r + 8 <= nd; r += 8) {
-    u2 x[8][4];
+  if constexpr (INFL == 0) {
+    for (; r + 8 <= nd; r += 8) {
+      u2 x[8][QL];
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
+      for (int q = 0; q < 8; ++q)
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        x[q][k] = ld_stream(reinterpret_cast<const u2*>(replica(S, r + q) + t0 + k * kBlock * 4 + lane4));
+        for (int k = 0; k < QL; ++k)
+          x[q][k] = ld_stream(reinterpret_cast<const u2*>(replica(S, r + q) + t0 + k * kBlock * 4 + lane4));
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
+      for (int q = 0; q < 8; ++q)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) accumulate4<SRC>(acc[k], x[q][k]);
+        for (int k = 0; k < QL; ++k) accumulate4<SRC>(acc[k], x[q][k]);
+    }
   }
   for (; r < nd; ++r) {
-    u2 x[4];
+    const uint16_t* const c = replica(S, r) + t0 + lane4;
+    u2 x[QL];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) x[k] = ld_stream(reinterpret_cast<const u2*>(replica(S, r) + t0 + k * kBlock * 4 + lane4));
+    for (int k = 0; k < QL; ++k) {
+      x[k] = ld_stream(reinterpret_cast<const u2*>(c + k * kBlock * 4));
+      if constexpr (INFL > 0) bound_loads_in_flight<INFL>();
+    }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) accumulate4<SRC>(acc[k], x[k]);
+    for (int k = 0; k < QL; ++k) accumulate4<SRC>(acc[k], x[k]);
   }
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
+  for (int k = 0; k < QL; ++k)
 #pragma unroll
     for (int q = 0; q < 4; ++q) a[k][q] = finish_average(acc[k][q], S);
 }
@@ -281,9 +306,10 @@ __device__ __forceinline__ void write_block_partial(double s, int bad, double* o
 //   kRedo: the second pass of a clipped optimistic step: exits unless
 //     state->redo; as kOptimistic with the clip multiplier, no partials.
 // VEC: fp32 arrays 16-byte and 16-bit copies 8-byte aligned (quad path).
+// QL: quads per lane, so tiles of kBlock * QL * 4 elements (see tile_quads).
 // ------------------------------------------------------------------------
 
-template <int SRC, bool VEC, int MODE>
+template <int SRC, bool VEC, int MODE, int QL>
 __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs A) {
   constexpr bool CHECKED = MODE == kChecked;
   constexpr bool REDO = MODE == kRedo;
@@ -316,7 +342,8 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs A) {
   const int pdt = A.param_dt;
   uint16_t* const param = static_cast<uint16_t*>(A.param);
   const int64_t n = A.n;
-  const int64_t ntiles = (n + kTile - 1) / kTile;
+  constexpr int64_t T = static_cast<int64_t>(kBlock) * QL * 4;
+  const int64_t ntiles = (n + T - 1) / T;
 
   auto one = [&](int64_t j) {
     const float a = source1<SRC>(A.src, j);
@@ -359,19 +386,18 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs A) {
 
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
     if constexpr (VEC && SRC != kSrcAvg) {
-      // several copies, a full tile: read them copy by copy (source16)
-      if (A.src.n_d > 1 && (t + 1) * kTile <= n) {
-        float a16[4][4];
-        source16<SRC>(A.src, t * kTile, a16);
+      // several copies, a full tile: read them copy by copy
+      if (A.src.n_d > 1 && (t + 1) * T <= n) {
+        float at[QL][4];
+        source_tile<SRC, QL, tile_inflight(QL)>(A.src, t * T, at);
 #pragma unroll
-        for (int k = 0; k < kQuadsPerThread; ++k)
-          quad(t * kTile + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4, a16[k]);
+        for (int k = 0; k < QL; ++k) quad(t * T + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4, at[k]);
         continue;
       }
     }
 #pragma unroll
-    for (int k = 0; k < kQuadsPerThread; ++k) {
-      const int64_t e = t * kTile + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4;
+    for (int k = 0; k < QL; ++k) {
+      const int64_t e = t * T + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4;
       if (VEC && e + 4 <= n) {
         float a[4];
         source4<SRC>(A.src, e, a);
@@ -390,33 +416,34 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs A) {
 // (if avg_out) and the norm / overflow partials.
 // ------------------------------------------------------------------------
 
-template <int SRC, bool VEC>
+template <int SRC, bool VEC, int QL>
 __global__ void __launch_bounds__(kBlock) reduce_kernel(const ReduceArgs R) {
   const float inv_scale = static_cast<float>(1.0 / static_cast<double>(R.state->loss_scale));
   double sumsq = 0.0;
   int bad = 0;
   float* const out = R.avg_out;
   const int64_t n = R.n;
-  const int64_t ntiles = (n + kTile - 1) / kTile;
+  constexpr int64_t T = static_cast<int64_t>(kBlock) * QL * 4;
+  const int64_t ntiles = (n + T - 1) / T;
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
     if constexpr (VEC) {
-      // several copies, a full tile: read them copy by copy (source16)
-      if (R.src.n_d > 1 && (t + 1) * kTile <= n) {
-        float a16[4][4];
-        source16<SRC>(R.src, t * kTile, a16);
+      // several copies, a full tile: read them copy by copy
+      if (R.src.n_d > 1 && (t + 1) * T <= n) {
+        float at[QL][4];
+        source_tile<SRC, QL, tile_inflight(QL)>(R.src, t * T, at);
 #pragma unroll
-        for (int k = 0; k < kQuadsPerThread; ++k) {
-          const int64_t e = t * kTile + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4;
+        for (int k = 0; k < QL; ++k) {
+          const int64_t e = t * T + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) account(a16[k][q], a16[k][q] * inv_scale, sumsq, bad);
-          if (out) st_stream(reinterpret_cast<f4*>(out + e), (f4){a16[k][0], a16[k][1], a16[k][2], a16[k][3]});
+          for (int q = 0; q < 4; ++q) account(at[k][q], at[k][q] * inv_scale, sumsq, bad);
+          if (out) st_stream(reinterpret_cast<f4*>(out + e), (f4){at[k][0], at[k][1], at[k][2], at[k][3]});
         }
         continue;
       }
     }
 #pragma unroll
-    for (int k = 0; k < kQuadsPerThread; ++k) {
-      const int64_t e = t * kTile + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4;
+    for (int k = 0; k < QL; ++k) {
+      const int64_t e = t * T + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4;
       if (VEC && e + 4 <= n) {
         float a[4];
         source4<SRC>(R.src, e, a);
@@ -673,39 +700,50 @@ __global__ void __launch_bounds__(kBlock) restore_kernel(const RestoreArgs R) {
   }
 }
 
-template <int SRC, bool VEC, int MODE>
-hipError_t adam_launch(const AdamArgs& a, hipStream_t s) {
-  int grid = stream_grid(a.n);
+template <int SRC, bool VEC, int MODE, int QL>
+hipError_t adam_launch(const AdamArgs& a, hipStream_t s, int* blocks) {
+  int grid = stream_grid(a.n, QL);
   if (MODE == kRedo && grid > kRedoGrid) grid = kRedoGrid;
-  hipLaunchKernelGGL((adam_kernel<SRC, VEC, MODE>), dim3(grid), dim3(kBlock), 0, s, a);
+  *blocks = grid;
+  hipLaunchKernelGGL((adam_kernel<SRC, VEC, MODE, QL>), dim3(grid), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
-template <int SRC, bool VEC>
-hipError_t reduce_launch(const ReduceArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((reduce_kernel<SRC, VEC>), dim3(stream_grid(a.n)), dim3(kBlock), 0, s, a);
+template <int SRC, bool VEC, int QL>
+hipError_t reduce_launch(const ReduceArgs& a, hipStream_t s, int* blocks) {
+  *blocks = stream_grid(a.n, QL);
+  hipLaunchKernelGGL((reduce_kernel<SRC, VEC, QL>), dim3(*blocks), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_adam(const AdamArgs& a, int src, bool vec, int mode, hipStream_t s) {
-#define ZDP_ADAM_MODE(SRC, VEC)                                               \
-  switch (mode) {                                                             \
-    case kFused: return adam_launch<SRC, VEC, kFused>(a, s);                  \
-    case kChecked: return adam_launch<SRC, VEC, kChecked>(a, s);              \
-    case kOptimistic: return adam_launch<SRC, VEC, kOptimistic>(a, s);        \
-    case kRedo: return adam_launch<SRC, VEC, kRedo>(a, s);                    \
-    default: return hipErrorInvalidValue;                                     \
+hipError_t launch_adam(const AdamArgs& a, int src, bool vec, int mode, hipStream_t s, int* blocks) {
+  const bool wide = tile_quads(src, vec, a.src.n_d) == kQuadsWide;
+#define ZDP_ADAM_MODE(SRC, VEC, QL)                                                 \
+  switch (mode) {                                                                   \
+    case kFused: return adam_launch<SRC, VEC, kFused, QL>(a, s, blocks);            \
+    case kChecked: return adam_launch<SRC, VEC, kChecked, QL>(a, s, blocks);        \
+    case kOptimistic: return adam_launch<SRC, VEC, kOptimistic, QL>(a, s, blocks);  \
+    case kRedo: return adam_launch<SRC, VEC, kRedo, QL>(a, s, blocks);              \
+    default: return hipErrorInvalidValue;                                           \
   }
-#define ZDP_ADAM(SRC)                                                         \
-  if (src == SRC) {                                                           \
-    if (vec) { ZDP_ADAM_MODE(SRC, true) }                                     \
-    ZDP_ADAM_MODE(SRC, false)                                                 \
+#define ZDP_ADAM(SRC)                                                               \
+  if (src == SRC) {                                                                 \
+    if (vec) { ZDP_ADAM_MODE(SRC, true, kQuadsPerThread) }                          \
+    ZDP_ADAM_MODE(SRC, false, kQuadsPerThread)                                      \
+  }
+#define ZDP_ADAM_WIDE(SRC)                                                          \
+  if (src == SRC) { ZDP_ADAM_MODE(SRC, true, kQuadsWide) }
+  if (wide) {
+    ZDP_ADAM_WIDE(kSrcF16)
+    ZDP_ADAM_WIDE(kSrcBF16)
+    return hipErrorInvalidValue;
   }
   ZDP_ADAM(kSrcAvg)
   ZDP_ADAM(kSrcF16)
   ZDP_ADAM(kSrcBF16)
+#undef ZDP_ADAM_WIDE
 #undef ZDP_ADAM
 #undef ZDP_ADAM_MODE
   return hipErrorInvalidValue;
@@ -721,9 +759,15 @@ hipError_t launch_restore(const RestoreArgs& a, bool vec, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_reduce(const ReduceArgs& a, int src, bool vec, hipStream_t s) {
-  if (src == kSrcF16) return vec ? reduce_launch<kSrcF16, true>(a, s) : reduce_launch<kSrcF16, false>(a, s);
-  if (src == kSrcBF16) return vec ? reduce_launch<kSrcBF16, true>(a, s) : reduce_launch<kSrcBF16, false>(a, s);
+// The averaging pass keeps 4 quads per lane at every N_d: it has no state
+// streams, and the wide, capped read measured slower there.
+hipError_t launch_reduce(const ReduceArgs& a, int src, bool vec, hipStream_t s, int* blocks) {
+  if (src == kSrcF16)
+    return vec ? reduce_launch<kSrcF16, true, kQuadsPerThread>(a, s, blocks)
+               : reduce_launch<kSrcF16, false, kQuadsPerThread>(a, s, blocks);
+  if (src == kSrcBF16)
+    return vec ? reduce_launch<kSrcBF16, true, kQuadsPerThread>(a, s, blocks)
+               : reduce_launch<kSrcBF16, false, kQuadsPerThread>(a, s, blocks);
   return hipErrorInvalidValue;
 }
 

@@ -16,6 +16,15 @@ namespace zdp {
 constexpr int kBlock = 256;
 constexpr int kQuadsPerThread = 4;
 constexpr int kTile = kBlock * kQuadsPerThread * 4;  // elements per tile
+// With many gradient copies the update kernel's lanes take 8 quads (tiles of
+// 8192), so a block reads each copy in 16 KiB runs, and a wave keeps at most
+// kWideInflight gradient loads in flight; with fewer copies, and in the
+// averaging pass, 4 quads per lane and eight copies' loads at once. See
+// source_tile.
+constexpr int kQuadsWide = 8;
+constexpr int kWideCopies = 32;
+constexpr int kWideInflight = 3;
+constexpr int tile_inflight(int quads) { return quads == kQuadsWide ? kWideInflight : 0; }
 constexpr int kMaxGrid = 1 << 20;                    // blocks per launch (tiles beyond: grid-stride)
 constexpr int kInlineReplicas = 64;                  // replica pointers carried in the kernel arguments
 
@@ -128,17 +137,25 @@ enum StepMode { kFused = 0, kChecked = 1, kOptimistic = 2, kRedo = 3 };
 constexpr int kRedoGrid = 65536;
 constexpr int kScanGrid = 65536;  // blocks of the single-copy scan (each loops over tiles)
 
-// Blocks of a streaming launch over n elements.
-inline int stream_grid(int64_t n) {
-  int64_t tiles = (n + kTile - 1) / kTile;
+// Quads per lane of an update launch: the wide tile for the aligned path over
+// kWideCopies or more copies, else kQuadsPerThread.
+inline int tile_quads(int src_kind, bool vec, int n_d) {
+  return vec && src_kind != kSrcAvg && n_d >= kWideCopies ? kQuadsWide : kQuadsPerThread;
+}
+
+// Blocks of a streaming launch over n elements (tiles of kBlock * quads * 4).
+inline int stream_grid(int64_t n, int quads = kQuadsPerThread) {
+  const int64_t tile = static_cast<int64_t>(kBlock) * quads * 4;
+  int64_t tiles = (n + tile - 1) / tile;
   if (tiles < 1) tiles = 1;
   return static_cast<int>(tiles < kMaxGrid ? tiles : kMaxGrid);
 }
 
 // Launchers (kernels.hip). Each returns the hipError_t of its launches.
-// `vec` selects the aligned quad path.
-hipError_t launch_adam(const AdamArgs& a, int src_kind, bool vec, int mode, hipStream_t s);
-hipError_t launch_reduce(const ReduceArgs& a, int src_kind, bool vec, hipStream_t s);
+// `vec` selects the aligned quad path; *blocks receives the grid size, which is
+// the number of block partials the launch writes.
+hipError_t launch_adam(const AdamArgs& a, int src_kind, bool vec, int mode, hipStream_t s, int* blocks);
+hipError_t launch_reduce(const ReduceArgs& a, int src_kind, bool vec, hipStream_t s, int* blocks);
 // Single-copy scan (partials only) of a 16-byte-aligned copy; scan_grid(n) blocks, one partial each.
 hipError_t launch_scan(const ReduceArgs& a, int src_kind, hipStream_t s);
 int scan_grid(int64_t n);
