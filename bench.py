@@ -171,6 +171,15 @@ class Setup:
                 g.replicas, g.avg = reps[gi], None
 
 
+# what one step launches, per pipeline (the events bracket all of it)
+STEP_KERNELS = {
+    "fused": "adam_kernel (average, partials, Adam, writeback) + fold + 1-block finalize",
+    "checked": "reduce_kernel or scan_kernel (average / norm partials) + fold + finalize, then adam_kernel "
+               "+ commit",
+    "optimistic": "adam_kernel (into the second state set) + fold + finalize + restore (+ second pass when "
+                  "clipping)",
+}
+
 CPU_CHUNK = 1 << 24
 
 
@@ -314,7 +323,7 @@ def main():
         "pct_peak": 100.0 * achieved / PEAK_HBM_GBPS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
-                     "kernel": "adam_kernel (fused step) + 1-block finalize, HIP events per step",
+                     "kernel": STEP_KERNELS[pipeline] + ", HIP events around each step",
                      "kernel_ms": ev_mean, "algorithmic_bytes": algo_bytes},
         "cpu_baseline": cpu,
     }
