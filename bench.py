@@ -66,6 +66,9 @@ def parse():
     p.add_argument("--placement", choices=["regions", "packed"], default="regions",
                    help="buffers carved from one arena spread over HBM's 96 GiB regions (regions), or "
                         "one allocation each in order (packed)")
+    p.add_argument("--regions", type=int, default=0,
+                   help="regions placement: spread the buffers over exactly this many 96 GiB regions "
+                        "(0: the fewest, at least two, that hold them)")
     p.add_argument("--quiet", action="store_true")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="only run a plain device copy of BYTES bytes --steps times (to calibrate "
@@ -98,7 +101,8 @@ class Setup:
     buffers spread over its 96 GiB regions; the default) or "packed" (one
     allocation per buffer)."""
 
-    def __init__(self, wl, dev, optimistic=False, placement="regions", whole=True, max_grad_norm=0.0):
+    def __init__(self, wl, dev, optimistic=False, placement="regions", whole=True, max_grad_norm=0.0,
+                 n_regions=0):
         import zero_dp_partitioned_amd as zdp
         from zero_dp_partitioned_amd import layout
         from workloads import derive_seed, fill_normal_, torch_dtype
@@ -120,7 +124,7 @@ class Setup:
         spec_pipeline = "fused" if pipeline == "checked" and wl.n_d == 1 else pipeline
         specs = layout.step_specs(shards, wl.n_d, torch_dtype(wl.grad_dt), torch_dtype(wl.param_dt),
                                   spec_pipeline, table)
-        buf, self.placement = layout.allocate(specs, dev, placement, whole=whole)
+        buf, self.placement = layout.allocate(specs, dev, placement, whole=whole, n_regions=n_regions)
         for gi, (spec, (psi, off, n)) in enumerate(zip(wl.groups, shards)):
             master = buf[(gi, "master")][:n]
             fill_normal_(master, 0.02, derive_seed(wl.key, gi, "master"))
@@ -262,7 +266,7 @@ def main():
     wl = WORKLOADS[args.workload]
     log(args, f"workload {wl.key}: {wl.title}")
     setup = Setup(wl, dev, optimistic=args.pipeline == "optimistic", placement=args.placement,
-                  whole=args.arena == "whole", max_grad_norm=args.max_grad_norm)
+                  whole=args.arena == "whole", max_grad_norm=args.max_grad_norm, n_regions=args.regions)
     S = setup.shard
     bpp = bytes_per_param(wl.n_d)
     log(args, f"shard {S} params, {len(setup.groups)} group(s), {bpp} B/param, "

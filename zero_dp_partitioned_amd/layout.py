@@ -65,7 +65,7 @@ def copy_stride(n):
     return (n + 63) // 64 * 64
 
 
-def allocate(specs, device, placement="regions", reserve_bytes=4 << 30, whole=True):
+def allocate(specs, device, placement="regions", reserve_bytes=4 << 30, whole=True, n_regions=0):
     """({key: tensor}, info) for `specs`. With "regions" the dict also holds
     "arena" (the uint8 arena) and "free" (its unused (offset, bytes) ranges,
     see free_ranges) for carving the caller's other tensors with arena_view.
@@ -78,7 +78,9 @@ def allocate(specs, device, placement="regions", reserve_bytes=4 << 30, whole=Tr
     region into one physical one; it is also what `whole` falls back to if
     the whole-memory allocation fails (info["arena"] then says so). The space
     after the planned buffers stays free for the caller's other data. A step
-    under SMALL_STEP_BYTES gets a small arena in one region."""
+    under SMALL_STEP_BYTES gets a small arena in one region. `n_regions` > 0
+    asks the planner for exactly that many regions (0: the fewest, at least
+    two, that hold the buffers)."""
     import torch
     if placement not in PLACEMENTS:
         raise ValueError(f"unknown placement {placement!r}")
@@ -88,11 +90,11 @@ def allocate(specs, device, placement="regions", reserve_bytes=4 << 30, whole=Tr
     if placement == "regions":
         free, _ = torch.cuda.mem_get_info(device)
         # a step under SMALL_STEP_BYTES is bound by launch latency, not HBM: one region
-        n_regions = 1 if sum(sizes) < SMALL_STEP_BYTES else 0
+        small = not n_regions and sum(sizes) < SMALL_STEP_BYTES
         offs, regs, total = plan_arena(sizes, [s.traffic for s in specs], free - reserve_bytes,
-                                       n_regions=n_regions)
+                                       n_regions=1 if small else n_regions)
         arena = None
-        if whole and n_regions != 1:
+        if whole and not small:
             try:
                 arena = torch.empty((free - reserve_bytes) // ARENA_ALIGN * ARENA_ALIGN, dtype=torch.uint8,
                                     device=device)
