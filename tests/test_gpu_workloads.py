@@ -11,6 +11,7 @@
   (chunked, chunk sums added in order); the flag, skip verdict, step count and
   loss scale on every call.
 """
+import dataclasses
 import os
 from concurrent.futures import ThreadPoolExecutor
 
@@ -80,8 +81,8 @@ class Run:
     arena over HBM's regions, gradient copies as a pointer table) and the
     oracle's copy of the sampled coordinates."""
 
-    def __init__(self, key, full=False, optimistic=False, max_grad_norm=0.0):
-        self.wl = wl = WORKLOADS[key]
+    def __init__(self, key, full=False, optimistic=False, max_grad_norm=0.0, rank=None):
+        self.wl = wl = WORKLOADS[key] if rank is None else dataclasses.replace(WORKLOADS[key], rank=rank)
         self.full = full
         self.optimistic = optimistic
         self.max_grad_norm = max_grad_norm
@@ -258,6 +259,23 @@ def test_7_5b_nd64():
     print("[workload] 7.5b_nd64", flush=True)
     st = Run("7.5b_nd64").run(full_scan_calls=(1,))
     assert st.step == 10
+    _free()
+
+
+@pytest.mark.timeout(900)
+def test_7_5b_nd64_rank0():
+    # rank 0: offset 0, every buffer 16-byte aligned (rank 63's parameter slice is only 8-byte aligned)
+    print("[workload] 7.5b_nd64 rank 0", flush=True)
+    st = Run("7.5b_nd64", rank=0).run(steps=3, full_scan_calls=(1,))
+    assert st.step == 3
+    _free()
+
+
+@pytest.mark.timeout(900)
+def test_13b_nd8_rank0():
+    print("[workload] 13b_nd8 rank 0 (checked)", flush=True)
+    st = Run("13b_nd8", rank=0).run(steps=5, full_scan_calls=(1,))
+    assert st.step == 4 and st.loss_scale == 32768.0
     _free()
 
 
