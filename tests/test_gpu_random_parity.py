@@ -3,8 +3,9 @@ the oracle, bit for bit, three calls each. Each case draws 1-3 groups (shard
 length 1..40,000, or 1.5M..6M in the large cases, N_d per group from 1-9, 64 or 65, parameter offset and
 alignment, unaligned fp32 state), a gradient dtype, a copy layout (pointer
 table, equally spaced buffer, packed unaligned), a pipeline (fused, checked,
-optimistic) with or without clipping, a loss scale, and an inf or NaN written
-into a copy now and then."""
+optimistic) with or without clipping, a loss scale, an inf or NaN written
+into a copy now and then, and the parameter vector's dtype (the gradients'
+most of the time, the other 16-bit type, or no fused writeback at all)."""
 import numpy as np
 import pytest
 import torch
@@ -43,7 +44,8 @@ def _case(seed, large=False):
     total = sum(g["n"] / g["n_d"] for g in groups)
     max_norm = 1e-3 * np.sqrt(total) * float(rng.uniform(0.5, 2.0)) if clip else 0.0
     inject = [bool(rng.random() < 0.25) for _ in range(3)]
-    return dt, pipeline, clip, groups, scale, max_norm, inject
+    pdt = [dt, dt, dt, {"f16": "bf16", "bf16": "f16"}[dt], None][rng.integers(5)]
+    return dt, pipeline, clip, groups, scale, max_norm, inject, pdt
 
 
 @pytest.mark.parametrize("seed", range(N_CASES))
@@ -57,11 +59,13 @@ def test_random_large_configuration(seed):
 
 
 def run_case(seed, case):
-    dt, pipeline, clip, specs, scale, max_norm, inject = case
+    dt, pipeline, clip, specs, scale, max_norm, inject, pdt = case
     dynamic = pipeline != "fused" and (pipeline == "optimistic" or seed % 2 == 0)
-    tag = f"seed {seed}: {dt} {pipeline} dynamic={dynamic} clip={max_norm:.3g} scale={scale} groups={specs}"
+    tag = (f"seed {seed}: {dt} params {pdt} {pipeline} dynamic={dynamic} clip={max_norm:.3g} scale={scale} "
+           f"groups={specs}")
     print(f"[case] {tag}", flush=True)
     odt = ORACLE_DT[dt]
+    opdt = ORACLE_DT[pdt] if pdt else odt
     pol = oracle.Policy(skip_on_overflow=dynamic, growth_interval=2, max_grad_norm=max_norm)
     sc = (zdp.policy(dynamic, growth_interval=2, max_grad_norm=max_norm, optimistic=pipeline == "optimistic")
           if pipeline != "fused" else None)
@@ -72,8 +76,8 @@ def run_case(seed, case):
     for gi, g in enumerate(specs):
         n, off, mis = g["n"], g["off"], g["mis"]
         master0 = normal_f32_np(n, 0.02, (40, seed, gi, "master"))
-        flat0 = to16_bits_np(normal_f32_np(off + n + 3, 0.02, (40, seed, gi, "flat")), dt)
-        flat0[off:off + n] = to16_bits_np(master0, dt)
+        flat0 = to16_bits_np(normal_f32_np(off + n + 3, 0.02, (40, seed, gi, "flat")), pdt or dt)
+        flat0[off:off + n] = to16_bits_np(master0, pdt or dt)
 
         def fp32(x=None):
             t = carve(n + 8, mis, n, torch.float32)
@@ -82,11 +86,11 @@ def run_case(seed, case):
         alt = {}
         if pipeline == "optimistic":
             alt = dict(master_alt=fp32(), exp_avg_alt=fp32(), exp_avg_sq_alt=fp32())
-        grps.append(zdp.Group(fp32(master0), fp32(), fp32(), flat_param=up16(flat0, dt), param_offset=off,
-                              weight_decay=g["wd"], **alt))
+        grps.append(zdp.Group(fp32(master0), fp32(), fp32(), flat_param=up16(flat0, pdt) if pdt else None,
+                              param_offset=off if pdt else 0, weight_decay=g["wd"], **alt))
         ogs.append(oracle.Group(replicas=None, grad_dt=odt, master=master0.copy(), m=np.zeros(n, np.float32),
-                                v=np.zeros(n, np.float32), param=flat0[off:off + n].copy(), param_dt=odt,
-                                weight_decay=g["wd"]))
+                                v=np.zeros(n, np.float32), param=flat0[off:off + n].copy() if pdt else None,
+                                param_dt=opdt, weight_decay=g["wd"]))
         flats0.append(flat0)
     ws, st = zdp.new_workspace(len(specs)), zdp.new_state(scale)
     ost = oracle.State(loss_scale=scale)
@@ -126,6 +130,8 @@ def run_case(seed, case):
         for gi, (g, og, spec) in enumerate(zip(grps, ogs, specs)):
             cm, cmm, cv = zdp.current_state(g, s)
             _compare_group(f"{tag} call {k + 1} group {gi}", cm, cmm, cv, og)
+            if pdt is None:
+                continue
             got = down16(g.flat_param)
             off, n = spec["off"], spec["n"]
             assert_u16_equal(got[off:off + n], og.param, f"{tag} call {k + 1} group {gi} param")
