@@ -1,4 +1,4 @@
-"""Random parity sweep: seeded random configurations of the whole step against
+"""Random parity sweep: 1,000 seeded random configurations (and 24 large ones) of the whole step against
 the oracle, bit for bit, three calls each. Each case draws 1-3 groups (shard
 length 1..40,000, or 1.5M..6M in the large cases, N_d per group from 1-9, 64 or 65, parameter offset and
 alignment, unaligned fp32 state), a gradient dtype, a copy layout (pointer
@@ -19,10 +19,10 @@ from test_gpu_parity import NEG_NAN, POS_INF, _compare_group, _compare_state, _r
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 200
+N_CASES = 1000
 
 
-N_LARGE = 16
+N_LARGE = 24
 
 
 def _case(seed, large=False):
