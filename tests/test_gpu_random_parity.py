@@ -1,6 +1,6 @@
 """Random parity sweep: 1,000 seeded random configurations (and 24 large ones) of the whole step against
 the oracle, bit for bit, three calls each. Each case draws 1-3 groups (shard
-length 1..40,000, or 1.5M..6M in the large cases, N_d per group from 1-9, 64 or 65, parameter offset and
+length 1..40,000, or 1.5M..6M in the large cases, N_d per group from 1-9, 32, 48, 64 or 65, parameter offset and
 alignment, unaligned fp32 state), a gradient dtype, a copy layout (pointer
 table, equally spaced buffer, packed unaligned), a pipeline (fused, checked,
 optimistic) with or without clipping, a loss scale, an inf or NaN written
@@ -36,7 +36,7 @@ def _case(seed, large=False):
             n, n_d = int(rng.integers(1_500_000, 6_000_000)), int(rng.choice([1, 2, 4, 8]))
         else:
             n = int(rng.choice([1, 7, 8, 9, 255, 4096, 4097, int(rng.integers(1, 40_000))]))
-            n_d = int(rng.choice([1, 1, 2, 3, 4, 5, 8, 9, 64, 65]))
+            n_d = int(rng.choice([1, 1, 2, 3, 4, 5, 8, 9, 32, 48, 64, 65]))
         layout = "strided" if n_d > 64 else ["table", "strided", "packed"][rng.integers(3)]
         groups.append(dict(n=n, n_d=n_d, layout=layout, off=int(rng.integers(0, 9)),
                            mis=int(rng.choice([0, 0, 0, 1, 2])), wd=float(rng.choice([0.0, 0.1]))))
