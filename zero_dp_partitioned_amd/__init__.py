@@ -198,8 +198,15 @@ def _torch():
     return torch
 
 
+_DTYPES = {}
+
+
 def _dt(t):
+    code = _DTYPES.get(t.dtype)
+    if code is not None:
+        return code
     torch = _torch()
+    _DTYPES.update({torch.float16: DT_F16, torch.bfloat16: DT_BF16})
     if t.dtype == torch.float16:
         return DT_F16
     if t.dtype == torch.bfloat16:
@@ -221,8 +228,20 @@ def _nbytes(t):
     return t.numel() * t.element_size()
 
 
+_ARRAY_TYPES = {}
+
+
+def _array_type(ctype, n):
+    """ctype * n, built once per length (building the type costs more than filling it)."""
+    key = (ctype, n)
+    t = _ARRAY_TYPES.get(key)
+    if t is None:
+        t = _ARRAY_TYPES[key] = ctype * n
+    return t
+
+
 def _ptr_array(tensors):
-    return (ctypes.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
+    return _array_type(ctypes.c_void_p, len(tensors))(*[t.data_ptr() for t in tensors])
 
 
 def new_state(loss_scale=1.0, device="cuda", stream=None):
@@ -323,27 +342,24 @@ class Group:
     weight_decay: float = 0.0
 
 
-def _group_struct(g, keep):
-    s = _Group()
+def _group_struct(g, keep, s):
+    """Fill the zero-initialised zero_group `s` from Group `g`; arrays the
+    struct points into are appended to `keep` (alive until the call returns)."""
     n = g.master.numel()
     s.n = n
     if g.replicas is not None:
         arr = _ptr_array(g.replicas)
         keep.append(arr)
-        s.replicas = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+        s.replicas = arr
         s.n_d = len(g.replicas)
         s.grad_dt = _dt(g.replicas[0])
         for r in g.replicas:
             if r.numel() < n:
                 raise ValueError("replica shorter than the shard")
-    else:
-        s.replicas = None
-        s.n_d = 0
-        s.grad_dt = 0
-    s.avg = g.avg.data_ptr() if g.avg is not None else None
-    for name in ("exp_avg", "exp_avg_sq"):
-        if getattr(g, name).numel() != n:
-            raise ValueError(f"{name} length differs from master")
+    if g.avg is not None:
+        s.avg = g.avg.data_ptr()
+    if g.exp_avg.numel() != n or g.exp_avg_sq.numel() != n:
+        raise ValueError("exp_avg / exp_avg_sq length differs from master")
     s.master, s.exp_avg, s.exp_avg_sq = g.master.data_ptr(), g.exp_avg.data_ptr(), g.exp_avg_sq.data_ptr()
     if g.master_alt is not None:
         for name in ("master_alt", "exp_avg_alt", "exp_avg_sq_alt"):
@@ -352,25 +368,20 @@ def _group_struct(g, keep):
         s.master_alt = g.master_alt.data_ptr()
         s.exp_avg_alt = g.exp_avg_alt.data_ptr()
         s.exp_avg_sq_alt = g.exp_avg_sq_alt.data_ptr()
-    else:
-        s.master_alt = s.exp_avg_alt = s.exp_avg_sq_alt = None
     if g.flat_param is not None:
         if g.param_offset + n > g.flat_param.numel():
             raise ValueError("param_offset + n exceeds the flat parameter vector")
         s.flat_param = g.flat_param.data_ptr()
         s.param_offset = g.param_offset
         s.param_dt = _dt(g.flat_param)
-    else:
-        s.flat_param = None
-        s.param_offset = 0
-        s.param_dt = 0
     s.lr, s.beta1, s.beta2, s.eps, s.weight_decay = g.lr, g.beta1, g.beta2, g.eps, g.weight_decay
-    return s
 
 
 def adam_step(groups, workspace, state, policy_=None, stream=None):
     keep = []
-    arr = (_Group * len(groups))(*[_group_struct(g, keep) for g in groups])
+    arr = _array_type(_Group, len(groups))()
+    for g, s in zip(groups, arr):
+        _group_struct(g, keep, s)
     sc = ctypes.byref(policy_) if policy_ is not None else None
     _check(load().zero_adam_step(arr, len(groups), sc, _ptr(workspace), _nbytes(workspace), _ptr(state),
                                  _stream(stream)))
