@@ -416,7 +416,7 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs A) {
 // (if avg_out) and the norm / overflow partials.
 // ------------------------------------------------------------------------
 
-template <int SRC, bool VEC, int QL>
+template <int SRC, bool VEC, int QL, int INFL>
 __global__ void __launch_bounds__(kBlock) reduce_kernel(const ReduceArgs R) {
   const float inv_scale = static_cast<float>(1.0 / static_cast<double>(R.state->loss_scale));
   double sumsq = 0.0;
@@ -430,7 +430,7 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(const ReduceArgs R) {
       // several copies, a full tile: read them copy by copy
       if (R.src.n_d > 1 && (t + 1) * T <= n) {
         float at[QL][4];
-        source_tile<SRC, QL, tile_inflight(QL)>(R.src, t * T, at);
+        source_tile<SRC, QL, INFL>(R.src, t * T, at);
 #pragma unroll
         for (int k = 0; k < QL; ++k) {
           const int64_t e = t * T + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4;
@@ -709,10 +709,10 @@ hipError_t adam_launch(const AdamArgs& a, hipStream_t s, int* blocks) {
   return hipGetLastError();
 }
 
-template <int SRC, bool VEC, int QL>
+template <int SRC, bool VEC, int INFL>
 hipError_t reduce_launch(const ReduceArgs& a, hipStream_t s, int* blocks) {
-  *blocks = stream_grid(a.n, QL);
-  hipLaunchKernelGGL((reduce_kernel<SRC, VEC, QL>), dim3(*blocks), dim3(kBlock), 0, s, a);
+  *blocks = stream_grid(a.n, kQuadsPerThread);
+  hipLaunchKernelGGL((reduce_kernel<SRC, VEC, kQuadsPerThread, INFL>), dim3(*blocks), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
@@ -759,15 +759,19 @@ hipError_t launch_restore(const RestoreArgs& a, bool vec, hipStream_t s) {
   return hipGetLastError();
 }
 
-// The averaging pass keeps 4 quads per lane at every N_d: it has no state
-// streams, and the wide, capped read measured slower there.
+// The averaging pass keeps 4 quads per lane at every N_d (it has no state
+// streams, and the wide read measured slower there); from kCappedReduceCopies
+// copies up it caps the gradient loads in flight.
 hipError_t launch_reduce(const ReduceArgs& a, int src, bool vec, hipStream_t s, int* blocks) {
-  if (src == kSrcF16)
-    return vec ? reduce_launch<kSrcF16, true, kQuadsPerThread>(a, s, blocks)
-               : reduce_launch<kSrcF16, false, kQuadsPerThread>(a, s, blocks);
-  if (src == kSrcBF16)
-    return vec ? reduce_launch<kSrcBF16, true, kQuadsPerThread>(a, s, blocks)
-               : reduce_launch<kSrcBF16, false, kQuadsPerThread>(a, s, blocks);
+  const bool capped = vec && a.src.n_d >= kCappedReduceCopies;
+  if (src == kSrcF16) {
+    if (capped) return reduce_launch<kSrcF16, true, kWideInflight>(a, s, blocks);
+    return vec ? reduce_launch<kSrcF16, true, 0>(a, s, blocks) : reduce_launch<kSrcF16, false, 0>(a, s, blocks);
+  }
+  if (src == kSrcBF16) {
+    if (capped) return reduce_launch<kSrcBF16, true, kWideInflight>(a, s, blocks);
+    return vec ? reduce_launch<kSrcBF16, true, 0>(a, s, blocks) : reduce_launch<kSrcBF16, false, 0>(a, s, blocks);
+  }
   return hipErrorInvalidValue;
 }
 

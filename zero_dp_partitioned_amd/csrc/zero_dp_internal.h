@@ -25,6 +25,10 @@ constexpr int kQuadsWide = 8;
 constexpr int kWideCopies = 32;
 constexpr int kWideInflight = 3;
 constexpr int tile_inflight(int quads) { return quads == kQuadsWide ? kWideInflight : 0; }
+// The averaging pass (checked pipeline) keeps 4 quads per lane; from
+// kCappedReduceCopies copies up its waves also keep at most kWideInflight
+// gradient loads in flight (1-4 % faster there, no gain with fewer copies).
+constexpr int kCappedReduceCopies = 8;
 constexpr int kMaxGrid = 1 << 20;                    // blocks per launch (tiles beyond: grid-stride)
 constexpr int kInlineReplicas = 64;                  // replica pointers carried in the kernel arguments
 
