@@ -88,6 +88,9 @@ def allocate(specs, device, placement="regions", reserve_bytes=4 << 30, whole=Tr
     bufs = {}
     info = {"placement": placement}
     if placement == "regions":
+        # blocks torch has cached but not handed out count as used for the
+        # driver: return them first, so the arena spans all memory not in use
+        torch.cuda.empty_cache()
         free, _ = torch.cuda.mem_get_info(device)
         # a step under SMALL_STEP_BYTES is bound by launch latency, not HBM: one region
         small = not n_regions and sum(sizes) < SMALL_STEP_BYTES
