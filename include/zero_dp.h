@@ -141,6 +141,12 @@ typedef struct {
  * Writeback: flat_param (device, param_dt elements) receives the updated master
  *   rounded to 16 bits at elements [param_offset, param_offset + n); NULL skips
  *   it. Any 2-byte alignment of flat_param + param_offset is accepted.
+ * Speed: the fast path moves 4 elements per access; it needs master, exp_avg,
+ *   exp_avg_sq (and the *_alt set, and avg or every replica) to start at the
+ *   same offset modulo 4 elements, as views into flat buffers at one segment
+ *   offset do (up to 3 leading elements are then updated one by one). Arrays
+ *   at different offsets are still handled exactly, element by element, at
+ *   well under half the bandwidth.
  * Hyperparameters: lr, beta1, beta2, eps; weight_decay != 0 applies decoupled
  *   (AdamW) decay master *= (1 - lr * weight_decay) before the Adam update. */
 typedef struct {

@@ -30,6 +30,10 @@ def _replicas_on_device(reps, dt, layout):
     n = reps[0].size
     if layout == "table":
         return [up16(r, dt) for r in reps]
+    if layout.startswith("shift"):
+        # each copy in its own buffer, starting `shift` elements past an aligned address
+        k = int(layout[5:])
+        return [carve(n + 8, k, n, TORCH16[dt]).copy_(up16(r, dt)) for r in reps]
     # one buffer, copies equally spaced: padded to 64 elements ("strided") or
     # packed back to back so that most copies start unaligned ("packed")
     stride = ((n + 63) // 64) * 64 if layout == "strided" else n
@@ -125,6 +129,9 @@ FUSED_CASES = [
     (40_961, 32, "f16", 2, 0, "table"),         # 32+ copies: tiles of 8192, five full + a ragged tail
     (24_577, 48, "bf16", 0, 0, "table"),        # 48 copies: division by N_d, three wide tiles + tail
     (8_191, 32, "f16", 1, 0, "strided"),        # under one wide tile: the tail path only
+    (40_961, 4, "f16", 5, 1, "shift1"),         # every array 1 element past alignment: 3-element head, quads
+    (40_963, 32, "bf16", 2, 3, "shift3"),       # 3 past: 1-element head, then wide tiles
+    (3, 8, "f16", 0, 1, "shift1"),              # a shard shorter than its head
     (50_000, 8, "f16", 0, 0, "packed"),         # unaligned copies: element path
     (50_001, 2, "bf16", 0, 1, "table"),         # unaligned fp32 state: element path
     (4_500_001, 1, "bf16", 0, 0, "table"),      # more than one grid-stride round
@@ -310,13 +317,15 @@ def test_cast_writeback(dt, off):
 
 
 @pytest.mark.parametrize("n_d,dt,layout", [(1, "bf16", "table"), (4, "f16", "table"), (64, "f16", "strided"),
-                                           (3, "bf16", "packed"), (100, "f16", "strided")])
+                                           (3, "bf16", "packed"), (100, "f16", "strided"), (8, "f16", "shift2"),
+                                           (1, "bf16", "shift1")])
 def test_reduce_grad_segment(n_d, dt, layout):
     n = 70_001
     reps = [grads16_np(n, dt, 1.0, (11, r)) for r in range(n_d)]
     reps[0] = reps[0].copy()
     reps[0][5] = 0x8000   # -0
-    avg = torch.empty(n, dtype=torch.float32, device=DEV)
+    shift = int(layout[5:]) if layout.startswith("shift") else 0   # the average as far past alignment
+    avg = carve(n + 8, shift, n, torch.float32)
     ws, st = zdp.new_workspace(1), zdp.new_state(1.0)
     zdp.reduce_grad_segment(_replicas_on_device(reps, dt, layout), avg, ws, 0, st)
     zdp.grad_norm_overflow(None, ws, 1, st)

@@ -2,7 +2,8 @@
 the oracle, bit for bit, three calls each. Each case draws 1-3 groups (shard
 length 1..40,000, or 1.5M..6M in the large cases, N_d per group from 1-9, 32, 48, 64 or 65, parameter offset and
 alignment, unaligned fp32 state), a gradient dtype, a copy layout (pointer
-table, equally spaced buffer, packed unaligned), a pipeline (fused, checked,
+table, equally spaced buffer, packed unaligned, or each copy as far past
+alignment as the fp32 state, which the kernels peel as a short head), a pipeline (fused, checked,
 optimistic) with or without clipping, a loss scale, an inf or NaN written
 into a copy now and then, and the parameter vector's dtype (the gradients'
 most of the time, the other 16-bit type, or no fused writeback at all)."""
@@ -37,7 +38,7 @@ def _case(seed, large=False):
         else:
             n = int(rng.choice([1, 7, 8, 9, 255, 4096, 4097, int(rng.integers(1, 40_000))]))
             n_d = int(rng.choice([1, 1, 2, 3, 4, 5, 8, 9, 32, 48, 64, 65]))
-        layout = "strided" if n_d > 64 else ["table", "strided", "packed"][rng.integers(3)]
+        layout = "strided" if n_d > 64 else ["table", "strided", "packed", "shift"][rng.integers(4)]
         groups.append(dict(n=n, n_d=n_d, layout=layout, off=int(rng.integers(0, 9)),
                            mis=int(rng.choice([0, 0, 0, 1, 2])), wd=float(rng.choice([0.0, 0.1]))))
     scale = float(rng.choice([1.0, 1024.0] + ([65536.0] if dt == "f16" else [2.0 ** 20])))
@@ -105,7 +106,8 @@ def run_case(seed, case):
                 reps[r] = reps[r].copy()
                 reps[r][(seed * 7919 + k) % spec["n"]] = (POS_INF if (seed + k) % 2 else NEG_NAN)[dt]
             host.append(reps)
-            dev.append(_replicas_on_device(reps, dt, spec["layout"]))
+            lay = f"shift{spec['mis']}" if spec["layout"] == "shift" else spec["layout"]
+            dev.append(_replicas_on_device(reps, dt, lay))
         if checked:
             scans = []
             for gi, (g, spec) in enumerate(zip(grps, specs)):

@@ -42,6 +42,28 @@ int32_t align_class(const void* p) {
   return 2;
 }
 
+// The quad path loads fp32 arrays 16 bytes and 16-bit arrays 8 bytes at a
+// time, 4 elements either way. Arrays that all sit at the same offset modulo
+// 4 elements (views into flat buffers at one segment offset, say) reach that
+// alignment after the same number h < 4 of leading elements: the kernels
+// update those h elements one by one and the rest on the quad path. HeadCheck
+// collects the arrays of one launch; head() is that h, or -1 if they disagree
+// (then every element takes the element path).
+class HeadCheck {
+ public:
+  void add(const void* p, int64_t elem_bytes) {
+    const uintptr_t u = reinterpret_cast<uintptr_t>(p);
+    const int64_t h = (4 - static_cast<int64_t>((u / elem_bytes) % 4)) % 4;
+    if (h_ == kUnset) h_ = h;
+    else if (h_ != h) h_ = kMixed;
+  }
+  int64_t head() const { return h_ == kUnset ? 0 : h_; }
+
+ private:
+  static constexpr int64_t kUnset = -2, kMixed = -1;
+  int64_t h_ = kUnset;
+};
+
 // The device must be gfx950; checked once per device.
 int check_device() {
   static std::mutex mu;
@@ -310,7 +332,11 @@ int zero_reduce_grad_segment(const void* const* replicas, int32_t n_d, int32_t g
   bool vec = false;
   if (int rc = make_source(replicas, n_d, grad_dt, n, &R.src, &vec)) return rc;
   if (int rc = check_device()) return rc;
-  vec = vec && aligned(avg_out, 16);
+  HeadCheck hc;
+  hc.add(avg_out, 4);
+  for (int32_t r = 0; r < n_d && n > 0; ++r) hc.add(replicas[r], 2);
+  vec = hc.head() >= 0;
+  R.head = vec ? std::min<int64_t>(hc.head(), n) : 0;
   R.n = n;
   R.avg_out = avg_out;
   R.state = state;
@@ -346,6 +372,10 @@ int zero_grad_norm_overflow(const void* const* grads, const int64_t* counts, int
       R[g].avg_out = nullptr;
       R[g].state = state;
       R[g].partials = scratch_of(workspace);
+      HeadCheck hc;
+      hc.add(grads[g], 2);
+      vec[g] = true;  // one array: a head of h < 4 elements always aligns it
+      R[g].head = std::min<int64_t>(hc.head(), counts[g]);
       scan[g] = true;
     }
   }
@@ -356,6 +386,7 @@ int zero_grad_norm_overflow(const void* const* grads, const int64_t* counts, int
     if (!scan[g]) continue;
     // 16-byte-aligned copies take the wide-load scan; others the streaming pass
     const bool wide = aligned(grads[g], 16);
+    if (wide) R[g].head = 0;
     int blocks = scan_grid(R[g].n);
     hipError_t e = wide ? launch_scan(R[g], src, s) : launch_reduce(R[g], src, vec[g], s, &blocks);
     if (e != hipSuccess) return hip_fail(e, "scan launch");
@@ -401,13 +432,18 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_policy
       return fail(ZERO_ERR_INVALID_ARG, "group %d: master/exp_avg/exp_avg_sq is NULL", g);
     if (!aligned(G.master, 4) || !aligned(G.exp_avg, 4) || !aligned(G.exp_avg_sq, 4))
       return fail(ZERO_ERR_ALIGNMENT, "group %d: fp32 state not 4-byte aligned", g);
-    bool v = aligned(G.master, 16) && aligned(G.exp_avg, 16) && aligned(G.exp_avg_sq, 16);
+    HeadCheck hc;
+    hc.add(G.master, 4);
+    hc.add(G.exp_avg, 4);
+    hc.add(G.exp_avg_sq, 4);
     if (optimistic) {
       if ((!G.master_alt || !G.exp_avg_alt || !G.exp_avg_sq_alt) && G.n > 0)
         return fail(ZERO_ERR_INVALID_ARG, "group %d: the optimistic pipeline needs the *_alt state set", g);
       if (!aligned(G.master_alt, 4) || !aligned(G.exp_avg_alt, 4) || !aligned(G.exp_avg_sq_alt, 4))
         return fail(ZERO_ERR_ALIGNMENT, "group %d: fp32 *_alt state not 4-byte aligned", g);
-      v = v && aligned(G.master_alt, 16) && aligned(G.exp_avg_alt, 16) && aligned(G.exp_avg_sq_alt, 16);
+      hc.add(G.master_alt, 4);
+      hc.add(G.exp_avg_alt, 4);
+      hc.add(G.exp_avg_sq_alt, 4);
       a.master_alt = G.master_alt;
       a.m_alt = G.exp_avg_alt;
       a.v_alt = G.exp_avg_sq_alt;
@@ -419,20 +455,22 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_policy
       a.src.avg = G.avg;
       a.src.n_d = 1;
       src[g] = kSrcAvg;
-      v = v && aligned(G.avg, 16);
+      hc.add(G.avg, 4);
     } else {
       bool rv = false;
       if (int rc = make_source(G.replicas, G.n_d, G.grad_dt, G.n, &a.src, &rv)) return rc;
       src[g] = G.grad_dt == ZERO_DT_BF16 ? kSrcBF16 : kSrcF16;
-      v = v && rv;
+      for (int32_t r = 0; r < G.n_d && G.n > 0; ++r) hc.add(G.replicas[r], 2);
     }
+    const bool v = hc.head() >= 0;
+    a.head = v ? std::min<int64_t>(hc.head(), G.n) : 0;
     if (G.flat_param && G.n > 0) {
       if (!valid_dt(G.param_dt)) return fail(ZERO_ERR_INVALID_ARG, "group %d: param dtype %d", g, G.param_dt);
       if (G.param_offset < 0) return fail(ZERO_ERR_INVALID_ARG, "group %d: param_offset < 0", g);
       if (!aligned(G.flat_param, 2)) return fail(ZERO_ERR_ALIGNMENT, "group %d: flat_param not 2-byte aligned", g);
       a.param = static_cast<uint16_t*>(G.flat_param) + G.param_offset;
       a.param_dt = G.param_dt;
-      a.param_align = align_class(a.param);
+      a.param_align = align_class(static_cast<uint16_t*>(a.param) + a.head);  // quads start at the head
     }
     if (!(G.lr >= 0.0) || !(G.beta1 >= 0.0 && G.beta1 < 1.0) || !(G.beta2 >= 0.0 && G.beta2 < 1.0) ||
         !(G.eps > 0.0) || !(G.weight_decay >= 0.0))
@@ -499,7 +537,7 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_policy
         R.n = A[g].n;
         R.param = A[g].param;
         R.param_dt = A[g].param_dt;
-        R.param_align = A[g].param_align;
+        R.param_align = align_class(A[g].param);  // the restore kernel starts its quads at element 0
         R.state = state;
         const bool rv = aligned(R.master, 16) && aligned(R.master_alt, 16);
         e = launch_restore(R, rv, s);

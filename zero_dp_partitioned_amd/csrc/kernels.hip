@@ -343,7 +343,8 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs A) {
   uint16_t* const param = static_cast<uint16_t*>(A.param);
   const int64_t n = A.n;
   constexpr int64_t T = static_cast<int64_t>(kBlock) * QL * 4;
-  const int64_t ntiles = (n + T - 1) / T;
+  const int64_t h = A.head;  // tiles start at element h (aligned for the quad path)
+  const int64_t ntiles = (n - h + T - 1) / T;
 
   auto one = [&](int64_t j) {
     const float a = source1<SRC>(A.src, j);
@@ -384,20 +385,22 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs A) {
     }
   };
 
+  if (blockIdx.x == 0 && threadIdx.x < h) one(threadIdx.x);
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int64_t t0 = h + t * T;
     if constexpr (VEC && SRC != kSrcAvg) {
       // several copies, a full tile: read them copy by copy
-      if (A.src.n_d > 1 && (t + 1) * T <= n) {
+      if (A.src.n_d > 1 && t0 + T <= n) {
         float at[QL][4];
-        source_tile<SRC, QL, tile_inflight(QL)>(A.src, t * T, at);
+        source_tile<SRC, QL, tile_inflight(QL)>(A.src, t0, at);
 #pragma unroll
-        for (int k = 0; k < QL; ++k) quad(t * T + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4, at[k]);
+        for (int k = 0; k < QL; ++k) quad(t0 + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4, at[k]);
         continue;
       }
     }
 #pragma unroll
     for (int k = 0; k < QL; ++k) {
-      const int64_t e = t * T + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4;
+      const int64_t e = t0 + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4;
       if (VEC && e + 4 <= n) {
         float a[4];
         source4<SRC>(A.src, e, a);
@@ -424,16 +427,23 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(const ReduceArgs R) {
   float* const out = R.avg_out;
   const int64_t n = R.n;
   constexpr int64_t T = static_cast<int64_t>(kBlock) * QL * 4;
-  const int64_t ntiles = (n + T - 1) / T;
+  const int64_t h = R.head;  // tiles start at element h (aligned for the quad path)
+  const int64_t ntiles = (n - h + T - 1) / T;
+  if (blockIdx.x == 0 && threadIdx.x < h) {
+    const float a = source1<SRC>(R.src, threadIdx.x);
+    account(a, a * inv_scale, sumsq, bad);
+    if (out) out[threadIdx.x] = a;
+  }
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int64_t t0 = h + t * T;
     if constexpr (VEC) {
       // several copies, a full tile: read them copy by copy
-      if (R.src.n_d > 1 && (t + 1) * T <= n) {
+      if (R.src.n_d > 1 && t0 + T <= n) {
         float at[QL][4];
-        source_tile<SRC, QL, INFL>(R.src, t * T, at);
+        source_tile<SRC, QL, INFL>(R.src, t0, at);
 #pragma unroll
         for (int k = 0; k < QL; ++k) {
-          const int64_t e = t * T + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4;
+          const int64_t e = t0 + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4;
 #pragma unroll
           for (int q = 0; q < 4; ++q) account(at[k][q], at[k][q] * inv_scale, sumsq, bad);
           if (out) st_stream(reinterpret_cast<f4*>(out + e), (f4){at[k][0], at[k][1], at[k][2], at[k][3]});
@@ -443,7 +453,7 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(const ReduceArgs R) {
     }
 #pragma unroll
     for (int k = 0; k < QL; ++k) {
-      const int64_t e = t * T + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4;
+      const int64_t e = t0 + static_cast<int64_t>(k * kBlock + threadIdx.x) * 4;
       if (VEC && e + 4 <= n) {
         float a[4];
         source4<SRC>(R.src, e, a);
@@ -702,7 +712,7 @@ __global__ void __launch_bounds__(kBlock) restore_kernel(const RestoreArgs R) {
 
 template <int SRC, bool VEC, int MODE, int QL>
 hipError_t adam_launch(const AdamArgs& a, hipStream_t s, int* blocks) {
-  int grid = stream_grid(a.n, QL);
+  int grid = stream_grid(a.n - a.head, QL);
   if (MODE == kRedo && grid > kRedoGrid) grid = kRedoGrid;
   *blocks = grid;
   hipLaunchKernelGGL((adam_kernel<SRC, VEC, MODE, QL>), dim3(grid), dim3(kBlock), 0, s, a);
@@ -711,7 +721,7 @@ hipError_t adam_launch(const AdamArgs& a, hipStream_t s, int* blocks) {
 
 template <int SRC, bool VEC, int INFL>
 hipError_t reduce_launch(const ReduceArgs& a, hipStream_t s, int* blocks) {
-  *blocks = stream_grid(a.n, kQuadsPerThread);
+  *blocks = stream_grid(a.n - a.head, kQuadsPerThread);
   hipLaunchKernelGGL((reduce_kernel<SRC, VEC, kQuadsPerThread, INFL>), dim3(*blocks), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }

@@ -70,6 +70,8 @@ struct AdamArgs {
   int32_t group;
   const zero_step_state* state;
   double* partials;  // one per block (fused and optimistic pipelines); null in the checked one
+  int64_t head;      // leading elements (0-3) block 0 updates one by one, so that the quad
+                     // path starts where every array is aligned (see aligned_head)
 };
 
 // Arguments of the average kernel (checked pipeline) and of the single-copy scan.
@@ -79,6 +81,7 @@ struct ReduceArgs {
   float* avg_out;  // null: scan only
   const zero_step_state* state;
   double* partials;
+  int64_t head;    // as AdamArgs::head
 };
 
 // Fold one launch's block partials into a group's level-2 partials, in a
