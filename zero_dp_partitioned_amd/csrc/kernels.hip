@@ -10,7 +10,9 @@
 // this sustains clearly more bandwidth for a read-modify-write stream than a
 // resident grid looping over the vector. With 32 or more gradient copies the
 // update kernel's lanes take 8 quads (8192-element tiles) and read the copies
-// one after another with a cap on the loads in flight (source_tile).
+// one after another with a cap on the loads in flight (source_tile). Arrays
+// that all start at the same offset modulo 4 elements run the quad path after
+// a head of up to 3 elements that block 0 updates one by one.
 //
 // Numerics follow the per-coordinate Adam update of the ZeRO reading notes
 // (second part, §3) in fp32 with one rounding per operation: fp-contract is off
