@@ -117,11 +117,10 @@ int check_policy(const zero_policy* p) {
 
 bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
-// Fill a GradSource from a host array of replica pointers. Sets *vec_ok to
-// whether every replica start is 8-byte aligned (the quad path loads four
-// 16-bit values at a time).
-// An empty shard (n == 0) reads nothing, so its pointers may be NULL.
-int make_source(const void* const* replicas, int32_t n_d, int32_t dt, int64_t n, GradSource* S, bool* vec_ok) {
+// Fill a GradSource from a host array of replica pointers (which path the
+// kernels take is HeadCheck's business). An empty shard (n == 0) reads
+// nothing, so its pointers may be NULL.
+int make_source(const void* const* replicas, int32_t n_d, int32_t dt, int64_t n, GradSource* S) {
   memset(S, 0, sizeof *S);
   if (!replicas) return fail(ZERO_ERR_INVALID_ARG, "replica pointer array is NULL");
   if (n_d < 1) return fail(ZERO_ERR_INVALID_ARG, "n_d = %d < 1", n_d);
@@ -130,14 +129,11 @@ int make_source(const void* const* replicas, int32_t n_d, int32_t dt, int64_t n,
   if (n == 0) {
     S->n_d = n_d;
     S->nd = static_cast<float>(n_d);
-    *vec_ok = true;
     return ZERO_OK;
   }
-  bool va = true;
   for (int32_t r = 0; r < n_d; ++r) {
     if (!replicas[r]) return fail(ZERO_ERR_INVALID_ARG, "replica %d is NULL", r);
     if (!aligned(replicas[r], 2)) return fail(ZERO_ERR_ALIGNMENT, "replica %d is not 2-byte aligned", r);
-    va = va && aligned(replicas[r], 8);
   }
   if (n_d <= kInlineReplicas) {
     for (int32_t r = 0; r < n_d; ++r) S->rep[r] = replicas[r];
@@ -160,7 +156,6 @@ int make_source(const void* const* replicas, int32_t n_d, int32_t dt, int64_t n,
   S->n_d = n_d;
   S->nd = static_cast<float>(n_d);
   S->inv_nd = is_pow2(n_d) ? 1.0f / static_cast<float>(n_d) : 0.0f;
-  *vec_ok = va;
   return ZERO_OK;
 }
 
@@ -329,13 +324,12 @@ int zero_reduce_grad_segment(const void* const* replicas, int32_t n_d, int32_t g
   if (int rc = check_workspace(workspace, workspace_bytes)) return rc;
   if (group < 0 || group >= ZERO_MAX_GROUPS) return fail(ZERO_ERR_WORKSPACE, "group %d out of range", group);
   ReduceArgs R;
-  bool vec = false;
-  if (int rc = make_source(replicas, n_d, grad_dt, n, &R.src, &vec)) return rc;
+  if (int rc = make_source(replicas, n_d, grad_dt, n, &R.src)) return rc;
   if (int rc = check_device()) return rc;
   HeadCheck hc;
   hc.add(avg_out, 4);
   for (int32_t r = 0; r < n_d && n > 0; ++r) hc.add(replicas[r], 2);
-  vec = hc.head() >= 0;
+  const bool vec = hc.head() >= 0;
   R.head = vec ? std::min<int64_t>(hc.head(), n) : 0;
   R.n = n;
   R.avg_out = avg_out;
@@ -367,7 +361,7 @@ int zero_grad_norm_overflow(const void* const* grads, const int64_t* counts, int
       if (!grads[g]) continue;
       if (counts[g] < 0) return fail(ZERO_ERR_INVALID_ARG, "counts[%d] < 0", g);
       const void* one[1] = {grads[g]};
-      if (int rc = make_source(one, 1, grad_dt, counts[g], &R[g].src, &vec[g])) return rc;
+      if (int rc = make_source(one, 1, grad_dt, counts[g], &R[g].src)) return rc;
       R[g].n = counts[g];
       R[g].avg_out = nullptr;
       R[g].state = state;
@@ -457,8 +451,7 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_policy
       src[g] = kSrcAvg;
       hc.add(G.avg, 4);
     } else {
-      bool rv = false;
-      if (int rc = make_source(G.replicas, G.n_d, G.grad_dt, G.n, &a.src, &rv)) return rc;
+      if (int rc = make_source(G.replicas, G.n_d, G.grad_dt, G.n, &a.src)) return rc;
       src[g] = G.grad_dt == ZERO_DT_BF16 ? kSrcBF16 : kSrcF16;
       for (int32_t r = 0; r < G.n_d && G.n > 0; ++r) hc.add(G.replicas[r], 2);
     }
