@@ -183,3 +183,58 @@ def test_loss_scale_is_unscaled_before_the_update(dt):
         np.testing.assert_array_equal(x.view(np.uint32), y.view(np.uint32))
     np.testing.assert_array_equal(a.param, b.param)
     assert sa.norm2 == sb.norm2
+
+
+def _decode64(bits, dt):
+    """16-bit patterns -> float64, independently of the oracle (numpy's binary16, bfloat16 by shifting)."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    if dt == "f16":
+        return bits.view(np.float16).astype(np.float64)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("dt,wd", [("bf16", 0.1), ("f16", 0.0)])
+def test_whole_step_against_float64_brute_force(dt, wd):
+    # the whole step -- average of the N_d copies, unscale, AdamW with bias correction, skip on an
+    # overflowing call with the scale halved, writeback -- recomputed in float64 from the definitions
+    # (the reading notes' per-coordinate Adam, the walkthrough's step() actions), against the oracle
+    # within the error fp32 arithmetic can add
+    n, n_d, steps, lr, b1, b2, eps = 3000, 4, 6, 1e-3, 0.9, 0.999, 1e-8
+    u = 2.0 ** -24
+    odt = oracle.F16 if dt == "f16" else oracle.BF16
+    scale = 1024.0
+    g = _group(n, n_d, dt, 61, scale=scale, wd=wd, param=np.zeros(n, np.uint16))
+    st = oracle.State(loss_scale=scale)
+    pol = oracle.Policy(skip_on_overflow=True, growth_interval=1000)
+    theta = g.master.astype(np.float64)
+    m = np.zeros(n)
+    v = np.zeros(n)
+    m_mag = np.zeros(n)      # the moment's recursion on absolute values: its rounding error scales with this
+    t, s = 0, scale
+    for k in range(steps):
+        g.replicas = [grads16_np(n, dt, s, seed=(62, k, r)) for r in range(n_d)]
+        if k == 2:
+            g.replicas[1] = g.replicas[1].copy()
+            g.replicas[1][123] = 0x7C00 if dt == "f16" else 0x7F80     # +inf in one copy
+        avg = sum(_decode64(r, dt) for r in g.replicas) / n_d
+        oracle.step([g], pol, st)
+        if not np.isfinite(avg).all():
+            s = max(s / 2, 1.0)                 # the step is void, the scale halves
+        else:
+            grad = avg / s
+            t += 1
+            theta = theta * (1 - lr * wd)
+            m = b1 * m + (1 - b1) * grad
+            m_mag = b1 * m_mag + (1 - b1) * np.abs(grad)
+            v = b2 * v + (1 - b2) * grad * grad
+            theta = theta - lr * (m / (1 - b1 ** t)) / (np.sqrt(v / (1 - b2 ** t)) + eps)
+        assert (st.step, st.loss_scale, st.skipped) == (t, s, int(k == 2)), k
+        # fp32 rounding: each step adds a few ulps of |theta| and of the update (lr times a ratio of
+        # order one, whose own error grows with the moments' by a few ulps per step); the moments
+        # carry a few ulps per step of the magnitude of their terms (m may cancel, v cannot)
+        tol_theta = (k + 1) * (3 * u * np.abs(theta) + 32 * (k + 2) * u * lr)
+        assert (np.abs(g.master - theta) <= tol_theta).all(), (k, np.abs(g.master - theta).max())
+        assert (np.abs(g.m - m) <= 4 * (k + 1) * u * m_mag + 1e-30).all(), k
+        assert (np.abs(g.v - v) <= 8 * (k + 1) * u * np.abs(v) + 1e-30).all(), k
+        np.testing.assert_array_equal(g.param, oracle.encode16(g.master, odt))
+    assert t == steps - 1
