@@ -12,7 +12,10 @@ parameter: the 16-bit copies read once, fp32 master/m/v read and written, the
 16-bit parameter written) and against MI355X's 8 TB/s, and the CPU oracle
 timed on a bounded sample of the same workload on this host.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt2_1.5b]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama3_8b]
+
+The default workload is the largest shard one GPU holds: LLaMA-3 8B at
+N_d = 1 (AdamW over two groups, 8,030,261,248 parameters, 224.85 GB per step).
 """
 import argparse
 import hashlib
@@ -25,7 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
-DEFAULT_WORKLOAD = "gpt2_1.5b"
+DEFAULT_WORKLOAD = "llama3_8b"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "zero_dp_partitioned_amd", "csrc", "kernels.hip")
 
@@ -49,14 +52,18 @@ def kernel_source_hash():
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--steps", type=int, default=25)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--cpu-sample", type=int, default=1 << 29,
-                   help="elements of the shard the CPU oracle steps once (0: skip)")
-    p.add_argument("--pipeline", choices=["checked", "optimistic"], default="checked",
-                   help="dynamic-loss-scale workloads: verdict before the update (checked) or an "
-                        "update into a second state set committed afterwards (optimistic)")
+                   help="elements of the shard the CPU oracle steps once on every thread of the CPU "
+                        "share (0: skip)")
+    p.add_argument("--cpu-single", type=int, default=1 << 28,
+                   help="elements of the shard the CPU oracle steps once on one thread")
+    p.add_argument("--pipeline", choices=["checked", "optimistic"], default="optimistic",
+                   help="dynamic-loss-scale workloads: an update into a second state set committed "
+                        "afterwards (optimistic, one pass) or the verdict before the update (checked, "
+                        "an extra pass over an fp32 average: 2*N_d + 34 bytes per parameter)")
     p.add_argument("--max-grad-norm", type=float, default=0.0,
                    help="clip the gradient to this global norm (0: off); selects the checked pipeline, or "
                         "with --pipeline optimistic on a dynamic-scale workload the optimistic one")
@@ -187,21 +194,43 @@ STEP_KERNELS = {
 CPU_CHUNK = 1 << 24
 
 
-def cpu_threads():
-    """Host threads for the CPU baseline: this process's CPU share (the
-    affinity mask, capped by OMP_NUM_THREADS when set), at most 16."""
-    n = len(os.sched_getaffinity(0))
+def cgroup_cpus():
+    """CPUs this process may use by its cgroup's CPU quota (cgroup v2
+    cpu.max, else v1 cfs_quota_us / cfs_period_us), or None when unlimited."""
+    try:
+        quota, period = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if quota != "max":
+            return max(1, int(int(quota) // int(period)))
+        return None
+    except (OSError, ValueError):
+        pass
+    try:
+        quota = int(open("/sys/fs/cgroup/cpu/cpu.cfs_quota_us").read())
+        period = int(open("/sys/fs/cgroup/cpu/cpu.cfs_period_us").read())
+        return max(1, quota // period) if quota > 0 and period > 0 else None
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_share():
+    """The host CPUs the CPU baseline runs on: every CPU of this process's
+    affinity mask, capped by the cgroup CPU quota when one is set and by an
+    explicit OMP_NUM_THREADS. Returns (threads, description of the counts)."""
+    affinity = len(os.sched_getaffinity(0))
+    quota = cgroup_cpus()
     env = os.environ.get("OMP_NUM_THREADS", "")
-    if env.isdigit() and int(env) > 0:
-        n = min(n, int(env))
-    return max(1, min(n, 16))
+    omp = int(env) if env.isdigit() and int(env) > 0 else None
+    threads = min(x for x in (affinity, quota, omp) if x is not None)
+    counts = {"affinity_cpus": affinity, "cgroup_quota_cpus": quota, "omp_num_threads": omp,
+              "os_cpu_count": os.cpu_count()}
+    return max(1, threads), counts
 
 
-def cpu_baseline(setup, sample, args):
-    """The CPU oracle as it stands, on the first `sample` elements of the first
-    group's shard, one step: over fixed 2^24-element chunks on a thread pool
-    of the host's CPU share (each chunk one oracle call), and on one thread
-    over the first chunk."""
+def cpu_baseline(setup, sample, single, args):
+    """The CPU oracle as it stands, one step over the first `sample` elements
+    of the first group's shard in fixed 2^24-element chunks (each chunk one
+    oracle call) on a thread pool of the host's CPU share, and one step over
+    the first `single` elements on one thread."""
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
@@ -212,6 +241,7 @@ def cpu_baseline(setup, sample, args):
     wl = setup.wl
     g = setup.groups[0]
     k = min(sample, g.master.numel())
+    k1 = min(single, k)
     odt = oracle.F16 if wl.grad_dt == "f16" else oracle.BF16
     reps = [r[:k].cpu().view(torch.int16).numpy().view(np.uint16) for r in g.replicas]
     master = g.master[:k].cpu().numpy()
@@ -227,20 +257,23 @@ def cpu_baseline(setup, sample, args):
         oracle.step([og], policy, oracle.State(loss_scale=wl.loss_scale))
 
     chunks = [(s, min(k, s + CPU_CHUNK)) for s in range(0, k, CPU_CHUNK)]
-    threads = cpu_threads()
-    log(args, f"cpu oracle: one step over {k} elements, {len(chunks)} chunks on {threads} threads")
-    t0 = time.perf_counter()
-    one(chunks[0])
-    one_thread = (chunks[0][1] - chunks[0][0]) / (time.perf_counter() - t0)
+    threads, counts = cpu_share()
+    log(args, f"cpu oracle: one step over {k} elements, {len(chunks)} chunks on {threads} threads "
+              f"({counts}); one thread over {k1}")
     t0 = time.perf_counter()
     with ThreadPoolExecutor(threads) as ex:
         list(ex.map(one, chunks))
     dt = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    one((0, k1))
+    dt1 = time.perf_counter() - t0
+    one_thread = k1 / dt1
     return {"value": k / dt, "unit": "params/s", "cores": threads, "kind": "oracle",
-            "single_thread_value": one_thread,
-            "sample": f"first {k} elements of the {wl.key} shard (N_d={wl.n_d}), one step, scalar C oracle "
-                      f"over {len(chunks)} chunks of {CPU_CHUNK} elements on {threads} threads ({dt:.1f} s); "
-                      f"one thread on one chunk: {one_thread:.3g} params/s"}
+            "single_thread_value": one_thread, **counts,
+            "sample": f"first {k} elements of the {wl.key} shard (N_d={wl.n_d}, group 0), one step, scalar C "
+                      f"oracle over {len(chunks)} chunks of {CPU_CHUNK} elements on {threads} threads "
+                      f"({dt:.1f} s); one thread over the first {k1} elements: {one_thread:.3g} params/s "
+                      f"({dt1:.1f} s)"}
 
 
 def main():
@@ -304,7 +337,7 @@ def main():
             traffic = rec.get("bytes_per_step")
     cpu = None
     if args.cpu_sample > 0:
-        cpu = cpu_baseline(setup, args.cpu_sample, args)
+        cpu = cpu_baseline(setup, args.cpu_sample, args.cpu_single, args)
     out = {
         "metric": "params updated/sec and achieved HBM GB/s (% peak) per sharded Adam step",
         "value": value,

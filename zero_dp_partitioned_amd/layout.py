@@ -76,7 +76,9 @@ def allocate(specs, device, placement="regions", reserve_bytes=4 << 30, whole=Tr
     regions. A smaller arena (whole=False: up to the end of the last buffer)
     is backed wherever the driver finds room, which can put every planned
     region into one physical one; it is also what `whole` falls back to if
-    the whole-memory allocation fails (info["arena"] then says so). The space
+    the whole-memory allocation fails. info["arena"] names the arena that was
+    obtained ("whole: ...", "sized: ...", "sized: FALLBACK ...", or "none:
+    ..." for packed placement). The space
     after the planned buffers stays free for the caller's other data. A step
     under SMALL_STEP_BYTES gets a small arena in one region. `n_regions` > 0
     asks the planner for exactly that many regions (0: the fewest, at least
@@ -97,13 +99,19 @@ def allocate(specs, device, placement="regions", reserve_bytes=4 << 30, whole=Tr
         offs, regs, total = plan_arena(sizes, [s.traffic for s in specs], free - reserve_bytes,
                                        n_regions=1 if small else n_regions)
         arena = None
-        if whole and not small:
+        if small:
+            info["arena"] = "sized: a step under 1 GiB, one region"
+        elif not whole:
+            info["arena"] = "sized: ends at the last planned buffer (asked for)"
+        else:
             try:
                 arena = torch.empty((free - reserve_bytes) // ARENA_ALIGN * ARENA_ALIGN, dtype=torch.uint8,
                                     device=device)
                 total = arena.numel()
+                info["arena"] = "whole: all free device memory but the reserve"
             except torch.cuda.OutOfMemoryError:
-                info["arena"] = "sized: the whole-memory arena could not be allocated"
+                info["arena"] = ("sized: FALLBACK, the whole-memory arena could not be allocated, so the "
+                                 "planned regions need not be physical ones")
         if arena is None:
             arena = torch.empty(total, dtype=torch.uint8, device=device)
         for s, o in zip(specs, offs):
@@ -113,6 +121,7 @@ def allocate(specs, device, placement="regions", reserve_bytes=4 << 30, whole=Tr
         bufs["arena"] = arena
         bufs["free"] = free_ranges(offs, sizes, total)
     else:
+        info["arena"] = "none: one allocation per buffer, wherever the driver finds room"
         for s in specs:
             bufs[s.key] = torch.empty(max(1, s.numel), dtype=s.dtype, device=device)
     return bufs, info
