@@ -1,6 +1,11 @@
 """The Python binding's marshalling, without a GPU: the zero_group structs it
 builds from torch tensors carry the right counts, dtypes and pointers, and its
-own length checks (which guard device writes the library cannot bound) fire."""
+own checks fire before any pointer reaches the library: length (the library
+cannot bound device writes), dtype (an fp32 array given as bf16 would be read
+and written at twice its size), device (a host pointer given to a kernel
+faults) and contiguity (a strided view would be read as if it were dense).
+The structs are built here against the CPU device so that they can be
+inspected; the device calls demand the state's GPU."""
 import ctypes
 
 import pytest
@@ -9,11 +14,14 @@ import torch
 import zero_dp_partitioned_amd as zdp
 
 
-def _structs(groups):
+CPU = torch.device("cpu")
+
+
+def _structs(groups, device=CPU):
     keep = []
     arr = zdp._array_type(zdp._Group, len(groups))()
     for g, s in zip(groups, arr):
-        zdp._group_struct(g, keep, s)
+        zdp._group_struct(g, keep, s, device)
     return arr, keep
 
 
@@ -57,13 +65,67 @@ def test_average_source_and_struct_reuse_across_calls():
 
 
 @pytest.mark.parametrize("break_it,msg", [
-    (lambda g: g.replicas.__setitem__(1, torch.zeros(999, dtype=torch.bfloat16)), "replica shorter"),
-    (lambda g: setattr(g, "exp_avg", torch.zeros(999)), "length differs"),
+    (lambda g: g.replicas.__setitem__(1, torch.zeros(999, dtype=torch.bfloat16)), "shorter than the shard"),
+    (lambda g: setattr(g, "exp_avg", torch.zeros(999)), "length 999 differs"),
     (lambda g: setattr(g, "param_offset", 13), "exceeds the flat parameter vector"),  # 1013 > 1012
+    (lambda g: setattr(g, "param_offset", -1), "exceeds the flat parameter vector"),
     (lambda g: setattr(g, "master_alt", torch.zeros(1000)), "exp_avg_alt missing"),
+    (lambda g: setattr(g, "avg", torch.zeros(999)), "shorter than the shard"),
+    (lambda g: setattr(g, "exp_avg_alt", torch.zeros(1001)) or setattr(g, "master_alt", torch.zeros(1000))
+     or setattr(g, "exp_avg_sq_alt", torch.zeros(1000)), "length 1001 differs"),
 ])
 def test_length_checks(break_it, msg):
     g = _group()
     break_it(g)
     with pytest.raises(ValueError, match=msg):
         _structs([g])
+
+
+@pytest.mark.parametrize("break_it,msg", [
+    (lambda g: setattr(g, "master", torch.zeros(1000, dtype=torch.bfloat16)), "master: dtype"),
+    (lambda g: setattr(g, "exp_avg", torch.zeros(1000, dtype=torch.float64)), "exp_avg: dtype"),
+    (lambda g: setattr(g, "exp_avg_sq", torch.zeros(1000, dtype=torch.float16)), "exp_avg_sq: dtype"),
+    (lambda g: setattr(g, "avg", torch.zeros(1000, dtype=torch.bfloat16)), "avg: dtype"),
+    (lambda g: (setattr(g, "master_alt", torch.zeros(1000, dtype=torch.bfloat16)),
+                setattr(g, "exp_avg_alt", torch.zeros(1000)), setattr(g, "exp_avg_sq_alt", torch.zeros(1000))),
+     "master_alt: dtype"),
+    (lambda g: g.replicas.__setitem__(0, torch.zeros(1000, dtype=torch.float32)), r"replicas\[0\]: dtype"),
+    (lambda g: g.replicas.__setitem__(2, torch.zeros(1002, dtype=torch.float16)), r"replicas\[2\]: dtype"),
+    (lambda g: setattr(g, "flat_param", torch.zeros(2000, dtype=torch.float32)), "flat_param: dtype"),
+])
+def test_dtype_checks(break_it, msg):
+    g = _group()
+    break_it(g)
+    with pytest.raises(TypeError, match=msg):
+        _structs([g])
+
+
+@pytest.mark.parametrize("break_it,msg", [
+    (lambda g: setattr(g, "master", torch.zeros(2000)[::2]), "master: not contiguous"),
+    (lambda g: setattr(g, "exp_avg_sq", torch.zeros(2000)[::2]), "exp_avg_sq: not contiguous"),
+    (lambda g: g.replicas.__setitem__(1, torch.zeros(2002, dtype=torch.bfloat16)[::2]), r"replicas\[1\]: not contiguous"),
+    (lambda g: setattr(g, "flat_param", torch.zeros(4000, dtype=torch.float16)[::2]), "flat_param: not contiguous"),
+])
+def test_contiguity_checks(break_it, msg):
+    g = _group()
+    break_it(g)
+    with pytest.raises(ValueError, match=msg):
+        _structs([g])
+
+
+def test_host_tensors_are_refused_for_a_device_step():
+    g = _group()
+    with pytest.raises(ValueError, match="master: tensor on cpu, expected cuda:0"):
+        _structs([g], device=torch.device("cuda", 0))
+    # the device calls take the device from the state, which must be a device tensor
+    st, ws = torch.zeros(ctypes.sizeof(zdp.StepState), dtype=torch.uint8), torch.zeros(64, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="state must be a device tensor"):
+        zdp.adam_step([g], ws, st)
+    with pytest.raises(ValueError, match="state must be a device tensor"):
+        zdp.reduce_grad_segment(g.replicas, torch.zeros(1000), ws, 0, st)
+    with pytest.raises(ValueError, match="state must be a device tensor"):
+        zdp.grad_norm_overflow(None, ws, 1, st)
+    with pytest.raises(ValueError, match="state must be a device tensor"):
+        zdp.state_init(st)
+    with pytest.raises(ValueError, match="master must be a device tensor"):
+        zdp.cast_writeback(torch.zeros(10), torch.zeros(10, dtype=torch.float16), 0)

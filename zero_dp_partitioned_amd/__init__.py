@@ -28,7 +28,8 @@ ARENA_ALIGN = 2 << 20
 
 EXPORTS = ("zero_partition", "zero_partition_tensors", "zero_workspace_bytes",
            "zero_last_error", "zero_state_init", "zero_reduce_grad_segment",
-           "zero_grad_norm_overflow", "zero_adam_step", "zero_cast_writeback", "zero_plan_arena")
+           "zero_grad_norm_overflow", "zero_adam_step", "zero_cast_writeback", "zero_plan_arena",
+           "zero_set_grid_limit")
 
 
 class ZeroError(RuntimeError):
@@ -121,6 +122,7 @@ def load():
         L.zero_adam_step.argtypes = [ctypes.POINTER(_Group), i32, ctypes.POINTER(Policy), vp, sz, vp, vp]
         L.zero_cast_writeback.argtypes = [vp, i64, vp, i64, i32, vp]
         L.zero_plan_arena.argtypes = [ctypes.POINTER(ArenaBuffer), i32, i64, i32, i64, ctypes.POINTER(i64)]
+        L.zero_set_grid_limit.argtypes = [i32]
         for name in EXPORTS:
             fn = getattr(L, name)
             if name not in ("zero_workspace_bytes", "zero_last_error"):
@@ -162,6 +164,11 @@ def partition_tensors(numels, n_d, rank, align_elems=1):
             for i in range(n_out.value)]
 
 
+def set_grid_limit(max_blocks):
+    """Cap the blocks of every streaming launch (0: no cap); for tests."""
+    _check(load().zero_set_grid_limit(int(max_blocks)))
+
+
 def workspace_bytes(n_groups):
     return int(load().zero_workspace_bytes(n_groups))
 
@@ -199,6 +206,15 @@ def _torch():
 
 
 _DTYPES = {}
+
+
+def _dt_code(dtype):
+    torch = _torch()
+    if dtype == torch.float16:
+        return DT_F16
+    if dtype == torch.bfloat16:
+        return DT_BF16
+    raise TypeError(f"16-bit dtype expected, got {dtype}")
 
 
 def _dt(t):
@@ -244,6 +260,61 @@ def _ptr_array(tensors):
     return _array_type(ctypes.c_void_p, len(tensors))(*[t.data_ptr() for t in tensors])
 
 
+def _f32():
+    return (_torch().float32,)
+
+
+def _half():
+    torch = _torch()
+    return (torch.float16, torch.bfloat16)
+
+
+def _need(t, name, dtypes, device, n=None, exact=False):
+    """Refuse a tensor the kernels would misread before its pointer reaches
+    the library: a dtype other than `dtypes`, another device than `device`
+    (a host pointer handed to a kernel faults), a non-contiguous view (read as
+    if it were contiguous), or fewer than `n` elements (exactly `n` with
+    `exact`): the library knows pointers and counts, not allocation sizes."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: a torch tensor is expected, got {type(t).__name__}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {' or '.join(str(d) for d in dtypes)}")
+    if t.device != device:
+        raise ValueError(f"{name}: tensor on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: not contiguous")
+    if n is not None:
+        if exact and t.numel() != n:
+            raise ValueError(f"{name}: length {t.numel()} differs from the shard's {n}")
+        if t.numel() < n:
+            raise ValueError(f"{name}: {t.numel()} elements, shorter than the shard's {n}")
+    return t
+
+
+def _state_device(state, workspace=None):
+    """The device of a step state (a device tensor of at least
+    sizeof(zero_step_state) bytes); the workspace must be on it too."""
+    torch = _torch()
+    if not isinstance(state, torch.Tensor) or not state.is_cuda:
+        raise ValueError("state must be a device tensor (from new_state)")
+    dev = state.device
+    _need(state, "state", (torch.uint8,), dev, ctypes.sizeof(StepState))
+    if workspace is not None:
+        _need(workspace, "workspace", (torch.uint8,), dev)
+    return dev
+
+
+def _same_half(tensors, name, device, n):
+    """16-bit tensors of one dtype, on `device`, each at least n elements."""
+    if not tensors:
+        raise ValueError(f"{name}: empty list")
+    first = _need(tensors[0], f"{name}[0]", _half(), device, n)
+    for r, t in enumerate(tensors[1:], 1):
+        _need(t, f"{name}[{r}]", (first.dtype,), device, n)
+    return first.dtype
+
+
 def new_state(loss_scale=1.0, device="cuda", stream=None):
     """Allocate and initialise a device zero_step_state (a uint8 tensor)."""
     torch = _torch()
@@ -253,6 +324,7 @@ def new_state(loss_scale=1.0, device="cuda", stream=None):
 
 
 def state_init(state, loss_scale=1.0, stream=None):
+    _state_device(state)
     _check(load().zero_state_init(_ptr(state), float(loss_scale), _stream(stream)))
 
 
@@ -293,10 +365,10 @@ def is_checked(policy_):
 
 def reduce_grad_segment(replicas, avg_out, workspace, group, state, stream=None):
     """Average N_d gradient copies (list of 16-bit tensors of equal length)."""
+    dev = _state_device(state, workspace)
+    _need(avg_out, "avg_out", _f32(), dev)
     n = avg_out.numel()
-    for r in replicas:
-        if r.numel() < n:
-            raise ValueError("replica shorter than the shard")
+    _same_half(list(replicas), "replicas", dev, n)
     arr = _ptr_array(replicas)
     _check(load().zero_reduce_grad_segment(arr, len(replicas), _dt(replicas[0]), n, _ptr(avg_out),
                                            _ptr(workspace), _nbytes(workspace), group, _ptr(state),
@@ -306,11 +378,13 @@ def reduce_grad_segment(replicas, avg_out, workspace, group, state, stream=None)
 def grad_norm_overflow(grads, workspace, n_groups, state, policy_=None, stream=None, grad_dtype=None):
     """Finalise the norm / overflow flag. ``grads``: None, or a list of n_groups
     entries (a 16-bit tensor to scan, or None for a slot already filled)."""
+    dev = _state_device(state, workspace)
     if grads is None:
         gp, cp, dt = None, None, DT_F16 if grad_dtype is None else grad_dtype
     else:
         if len(grads) != n_groups:
             raise ValueError("grads must have one entry per group")
+        _same_half([g for g in grads if g is not None], "grads", dev, 0)
         # an empty gradient still marks its slot for scanning: give it a
         # non-NULL address (never read, there are no elements)
         gp = (ctypes.c_void_p * n_groups)(*[
@@ -342,34 +416,37 @@ class Group:
     weight_decay: float = 0.0
 
 
-def _group_struct(g, keep, s):
-    """Fill the zero-initialised zero_group `s` from Group `g`; arrays the
+def _group_struct(g, keep, s, device):
+    """Fill the zero-initialised zero_group `s` from Group `g` after checking
+    every tensor's dtype, device (`device`), contiguity and length; arrays the
     struct points into are appended to `keep` (alive until the call returns)."""
+    f32 = _f32()
+    _need(g.master, "master", f32, device)
     n = g.master.numel()
     s.n = n
+    _need(g.exp_avg, "exp_avg", f32, device, n, exact=True)
+    _need(g.exp_avg_sq, "exp_avg_sq", f32, device, n, exact=True)
     if g.replicas is not None:
+        s.grad_dt = _dt_code(_same_half(list(g.replicas), "replicas", device, n))
         arr = _ptr_array(g.replicas)
         keep.append(arr)
         s.replicas = arr
         s.n_d = len(g.replicas)
-        s.grad_dt = _dt(g.replicas[0])
-        for r in g.replicas:
-            if r.numel() < n:
-                raise ValueError("replica shorter than the shard")
     if g.avg is not None:
+        _need(g.avg, "avg", f32, device, n)
         s.avg = g.avg.data_ptr()
-    if g.exp_avg.numel() != n or g.exp_avg_sq.numel() != n:
-        raise ValueError("exp_avg / exp_avg_sq length differs from master")
     s.master, s.exp_avg, s.exp_avg_sq = g.master.data_ptr(), g.exp_avg.data_ptr(), g.exp_avg_sq.data_ptr()
     if g.master_alt is not None:
         for name in ("master_alt", "exp_avg_alt", "exp_avg_sq_alt"):
-            if getattr(g, name) is None or getattr(g, name).numel() != n:
-                raise ValueError(f"{name} missing or of the wrong length")
+            if getattr(g, name) is None:
+                raise ValueError(f"{name} missing")
+            _need(getattr(g, name), name, f32, device, n, exact=True)
         s.master_alt = g.master_alt.data_ptr()
         s.exp_avg_alt = g.exp_avg_alt.data_ptr()
         s.exp_avg_sq_alt = g.exp_avg_sq_alt.data_ptr()
     if g.flat_param is not None:
-        if g.param_offset + n > g.flat_param.numel():
+        _need(g.flat_param, "flat_param", _half(), device)
+        if g.param_offset < 0 or g.param_offset + n > g.flat_param.numel():
             raise ValueError("param_offset + n exceeds the flat parameter vector")
         s.flat_param = g.flat_param.data_ptr()
         s.param_offset = g.param_offset
@@ -378,10 +455,11 @@ def _group_struct(g, keep, s):
 
 
 def adam_step(groups, workspace, state, policy_=None, stream=None):
+    dev = _state_device(state, workspace)
     keep = []
     arr = _array_type(_Group, len(groups))()
     for g, s in zip(groups, arr):
-        _group_struct(g, keep, s)
+        _group_struct(g, keep, s, dev)
     sc = ctypes.byref(policy_) if policy_ is not None else None
     _check(load().zero_adam_step(arr, len(groups), sc, _ptr(workspace), _nbytes(workspace), _ptr(state),
                                  _stream(stream)))
@@ -396,8 +474,13 @@ def current_state(group, state_dict):
 
 
 def cast_writeback(master, flat_param, offset, stream=None):
+    torch = _torch()
+    if not isinstance(master, torch.Tensor) or not master.is_cuda:
+        raise ValueError("master must be a device tensor")
+    _need(master, "master", _f32(), master.device)
+    _need(flat_param, "flat_param", _half(), master.device)
     n = master.numel()
-    if offset + n > flat_param.numel():
+    if offset < 0 or offset + n > flat_param.numel():
         raise ValueError("offset + n exceeds the flat parameter vector")
     _check(load().zero_cast_writeback(_ptr(master), n, _ptr(flat_param), offset, _dt(flat_param),
                                       _stream(stream)))
