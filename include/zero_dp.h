@@ -325,6 +325,21 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_policy
 int zero_cast_writeback(const float* master, int64_t n, void* flat_param, int64_t offset,
                         int32_t param_dt, void* stream);
 
+/* ---- testing --------------------------------------------------------------
+ * Not an operation of the pages. Caps the blocks of every streaming launch
+ * (update, second pass, averaging, scan, restore, cast) at max_blocks > 0, on
+ * top of each launch's own cap (2^20 tiles per launch; 65,536 blocks for the
+ * second pass and the scan; 1,024 for the restore). Every streaming kernel
+ * loops over the tiles its grid does not cover, so a small shard under a low
+ * cap runs the same grid-stride loops that otherwise only shards of billions
+ * of elements reach; tests use it to check those loops element by element.
+ * 0 removes the cap (the default). Elementwise results do not depend on it;
+ * the norm is the same sum of squares grouped into other partials (equal to
+ * within fp64 reassociation). Process-wide, for every device and thread; a
+ * launch on another thread while it changes sees either value.
+ * Errors: INVALID_ARG for max_blocks < 0. */
+int zero_set_grid_limit(int32_t max_blocks);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "zero_dp.h"
+#include "../../zero_dp_partitioned_amd/csrc/zero_dp_internal.h"
 
 static int failures = 0;
 #define EXPECT(cond)                                                 \
@@ -142,6 +143,12 @@ static void device_call_checks() {
   EXPECT(zero_cast_writeback((const float*)fake, 10, fake, -1, 1, nullptr) == ZERO_ERR_INVALID_ARG);
   EXPECT(zero_cast_writeback((const float*)0x100001, 10, fake, 0, 1, nullptr) == ZERO_ERR_ALIGNMENT);
   EXPECT(zero_cast_writeback((const float*)fake, 0, fake, 0, 1, nullptr) == ZERO_OK);  // nothing to write
+  // the test knob on the grid size: any cap >= 0 is taken, a negative one refused
+  EXPECT(zero_set_grid_limit(-1) == ZERO_ERR_INVALID_ARG);
+  EXPECT(zero_set_grid_limit(3) == ZERO_OK);
+  EXPECT(zdp::stream_grid(int64_t(1) << 40) == 3 && zdp::stream_grid(10) == 1);
+  EXPECT(zero_set_grid_limit(0) == ZERO_OK);
+  EXPECT(zdp::stream_grid(int64_t(1) << 40) == zdp::kMaxGrid && zdp::stream_grid(4097) == 2);
 }
 
 int main() {

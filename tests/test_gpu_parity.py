@@ -7,7 +7,10 @@ backoff and growth, several groups).
 Bar: fp32 master / m / v and the 16-bit parameters bit-identical to the
 oracle (NaN compared as NaN), the overflow flag, step count, skip verdict and
 loss scale exact, the fp64 gradient norm within 1e-10 relative (the two sides
-sum in different orders)."""
+sum in different orders). Clipped runs: the clip multiplier equal, or one
+fp32 ulp off (it is rounded from the two sides' norms), and then master / m /
+v within 1e-6 relative (5e-6 after the first step) and the parameters within
+one ulp from that call on (tests/_parity.py)."""
 import numpy as np
 import pytest
 import torch
@@ -18,6 +21,7 @@ from workloads import grads16_np, normal_f32_np, to16_bits_np
 
 from _gpu_helpers import (DEV, ORACLE_DT, TORCH16, assert_bits_equal, assert_u16_equal, carve,
                           down16, down32, up16, up32)
+from _parity import Bar
 
 pytestmark = pytest.mark.gpu
 
@@ -46,7 +50,14 @@ def _replicas_on_device(reps, dt, layout):
     return out
 
 
-def _compare_group(tag, master, m, v, og):
+def _compare_group(tag, master, m, v, og, bar=None):
+    """master / m / v against the oracle group: bit for bit, or at the bar of
+    a clipped run (tests/_parity.py) once its multipliers have differed."""
+    if bar is not None:
+        bar.state32(down32(master), og.master, f"{tag} master", "master")
+        bar.state32(down32(m), og.m, f"{tag} exp_avg", "m")
+        bar.state32(down32(v), og.v, f"{tag} exp_avg_sq", "v")
+        return
     got_master = down32(master)
     nan = np.isnan(og.master)
     assert (np.isnan(got_master) == nan).all(), f"{tag}: NaN positions of master differ"
@@ -55,14 +66,20 @@ def _compare_group(tag, master, m, v, og):
     assert_bits_equal(down32(v), og.v, f"{tag} exp_avg_sq")
 
 
-def _compare_state(tag, st, ost):
+def _compare_state(tag, st, ost, bar=None):
+    """The device state against the oracle's. With a bar (clipped runs) the
+    clip multipliers may differ by one fp32 ulp, which moves the bar from bit
+    identity to the tolerances; without one they must be equal."""
     s = zdp.read_state(st)
     assert s["step"] == ost.step, tag
     assert s["overflow"] == ost.overflow, tag
     assert s["skipped"] == ost.skipped, tag
     assert s["loss_scale"] == np.float32(ost.loss_scale), tag
     assert s["good_steps"] == ost.good_steps, tag
-    assert s["clip_coef"] == np.float32(ost.clip), tag
+    if bar is None:
+        assert s["clip_coef"] == np.float32(ost.clip), tag
+    else:
+        bar.clip(tag, s["clip_coef"], ost.clip, applied=not ost.skipped)
     if np.isfinite(ost.norm2):
         assert abs(s["grad_norm_sq"] - ost.norm2) <= NORM_RTOL * ost.norm2, (tag, s["grad_norm_sq"], ost.norm2)
         assert s["grad_norm"] == pytest.approx(np.sqrt(ost.norm2), rel=1e-6)
@@ -134,7 +151,7 @@ FUSED_CASES = [
     (3, 8, "f16", 0, 1, "shift1"),              # a shard shorter than its head
     (50_000, 8, "f16", 0, 0, "packed"),         # unaligned copies: element path
     (50_001, 2, "bf16", 0, 1, "table"),         # unaligned fp32 state: element path
-    (4_500_001, 1, "bf16", 0, 0, "table"),      # more than one grid-stride round
+    (4_500_001, 1, "bf16", 0, 0, "table"),      # 1,099 tiles (grid-stride rounds: test_grid_stride_rounds)
     (4_500_013, 3, "f16", 7, 0, "table"),
 ]
 
@@ -379,6 +396,7 @@ def test_checked_pipeline_with_clipping(n, n_d, dt, skip, max_norm, scale):
     og = oracle.Group(replicas=None, grad_dt=odt, master=master0.copy(), m=np.zeros(n, np.float32),
                       v=np.zeros(n, np.float32), param=flat0.copy(), param_dt=odt, weight_decay=0.1)
     ost = oracle.State(loss_scale=scale)
+    bar = Bar()
     clipped = 0
     for k in range(5):
         reps = [grads16_np(n, dt, ost.loss_scale, (13, "g", k, r)) for r in range(n_d)]
@@ -397,10 +415,10 @@ def test_checked_pipeline_with_clipping(n, n_d, dt, skip, max_norm, scale):
         og.replicas = reps
         oracle.step([og], pol, ost)
         torch.cuda.synchronize()
-        _compare_group(f"{tag} call {k + 1}", master, m, v, og)
-        _compare_state(f"{tag} call {k + 1}", st, ost)
+        _compare_state(f"{tag} call {k + 1}", st, ost, bar)
+        _compare_group(f"{tag} call {k + 1}", master, m, v, og, bar)
         clipped += ost.clip < 1.0
-    assert_u16_equal(down16(flat), og.param, tag + " param")
+    bar.param16(down16(flat), og.param, tag + " param")
     if max_norm < 1:
         assert clipped >= 4
     else:
@@ -590,6 +608,7 @@ def test_optimistic_pipeline_with_clipping(sizes, n_d, dt):
     ws, st = zdp.new_workspace(len(sizes)), zdp.new_state(1024.0)
     ost = oracle.State(loss_scale=1024.0)
     factors = [2.0, 0.5, 2.0, 0.5, 2.0, 0.5, 0.5, 2.0]   # draws above / below the threshold
+    bar = Bar()
     clipped = unclipped = 0
     for k, f in enumerate(factors):
         for gi, (g, og) in enumerate(zip(grps, ogs)):
@@ -602,14 +621,124 @@ def test_optimistic_pipeline_with_clipping(sizes, n_d, dt):
         zdp.adam_step(grps, ws, st, sc)
         oracle.step(ogs, pol, ost)
         torch.cuda.synchronize()
-        s = _compare_state(f"{tag} call {k + 1}", st, ost)
+        s = _compare_state(f"{tag} call {k + 1}", st, ost, bar)
         assert s["redo"] == 0
         for gi, (g, og) in enumerate(zip(grps, ogs)):
             cm, cmm, cv = zdp.current_state(g, s)
-            _compare_group(f"{tag} call {k + 1} group {gi}", cm, cmm, cv, og)
-            assert_u16_equal(down16(g.flat_param), og.param, f"{tag} call {k + 1} group {gi} param")
+            _compare_group(f"{tag} call {k + 1} group {gi}", cm, cmm, cv, og, bar)
+            bar.param16(down16(g.flat_param), og.param, f"{tag} call {k + 1} group {gi} param")
         if not ost.skipped:
             clipped += ost.clip < 1.0
             unclipped += ost.clip == 1.0
     assert ost.step == len(factors) - 1
     assert clipped >= 3 and unclipped >= 3, (clipped, unclipped)
+
+
+# --------------------------------------------------------------------------
+# grid-stride rounds: the block cap lowered (zero_set_grid_limit) so that the
+# loops which otherwise only billions of elements reach run on small shards,
+# every element against the oracle
+# --------------------------------------------------------------------------
+
+@pytest.fixture
+def grid_limit():
+    """Set the block cap for one test; removed afterwards, pass or fail."""
+    try:
+        yield zdp.set_grid_limit
+    finally:
+        zdp.set_grid_limit(0)
+
+
+GRID_ROUND_CASES = {
+    # the update kernel (4-quad tiles, N_d = 1 and 8; 8-quad tiles at N_d = 64; the 3-element head)
+    "fused n_d=1": lambda: run_fused(100_003, 1, "bf16", steps=2, seed=31),
+    "fused n_d=8": lambda: run_fused(70_001, 8, "f16", steps=2, param_off=3, seed=32),
+    "fused n_d=64 wide": lambda: run_fused(90_001, 64, "f16", steps=2, param_off=4, layout="strided", seed=33),
+    "fused head": lambda: run_fused(40_961, 4, "f16", steps=2, param_off=5, misalign=1, layout="shift1", seed=34),
+    # averaging pass + norm + checked update, with two overflowing calls
+    "checked n_d=8": lambda: test_checked_pipeline_skip_and_scale(50_001, 8, "f16", True),
+    # the single-copy scan (16-byte aligned) and the streaming pre-pass (2-byte aligned)
+    "scan aligned": lambda: test_checked_single_copy_prepass_two_groups(0),
+    "scan unaligned": lambda: test_checked_single_copy_prepass_two_groups(1),
+    # optimistic update with overflowing calls: the restore kernel's loop
+    "optimistic": lambda: test_optimistic_pipeline(70_001, 8, "f16", 3, 0),
+    # clipped optimistic steps: the second pass's loop
+    "optimistic clip": lambda: test_optimistic_pipeline_with_clipping((30_011,), 4, "f16"),
+    "optimistic clip wide": lambda: test_optimistic_pipeline_with_clipping((24_577, 9_001), 32, "f16"),
+    # clipping in the checked pipeline
+    "checked clip": lambda: test_checked_pipeline_with_clipping(60_001, 4, "f16", False, 0.02, 1.0),
+    # standalone average and cast
+    "average": lambda: test_reduce_grad_segment(8, "f16", "shift2"),
+    "cast": lambda: test_cast_writeback("bf16", 1),
+}
+
+
+@pytest.mark.parametrize("limit", [1, 3])
+@pytest.mark.parametrize("case", sorted(GRID_ROUND_CASES))
+def test_grid_stride_rounds(case, limit, grid_limit):
+    print(f"[case] grid limit {limit}: {case}", flush=True)
+    grid_limit(limit)
+    GRID_ROUND_CASES[case]()
+
+
+# --------------------------------------------------------------------------
+# finite copies whose fp32 sum overflows: the flag is taken on the average,
+# so two bf16 copies of 3e38 overflow (flagged; the step is voided under a
+# dynamic scale) while two fp16 copies of 65504 do not (131008 is finite)
+# --------------------------------------------------------------------------
+
+def _sum_overflow_copies(n, n_d, dt, k, seed):
+    reps = [grads16_np(n, dt, 1.0, (seed, "g", k, r)) for r in range(n_d)]
+    big = to16_bits_np(np.array([3e38 if dt == "bf16" else 65504.0], np.float32), dt)[0]
+    for r in (0, n_d - 1):
+        reps[r] = reps[r].copy()
+        reps[r][n // 3] = big
+    return reps
+
+
+@pytest.mark.parametrize("pipeline", ["fused", "checked", "optimistic"])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_finite_copies_whose_sum_overflows(pipeline, dt):
+    n, n_d, seed = 30_011, 4, 41
+    tag = f"sum overflow {dt} {pipeline}"
+    print(f"[case] {tag}", flush=True)
+    odt = ORACLE_DT[dt]
+    dynamic = pipeline != "fused"
+    pol = oracle.Policy(skip_on_overflow=dynamic, growth_interval=1000)
+    sc = zdp.policy(True, optimistic=pipeline == "optimistic") if dynamic else None
+    master0 = normal_f32_np(n, 0.02, (seed, "master"))
+    flat0 = to16_bits_np(master0, dt)
+    mk = lambda x=None: up32(x) if x is not None else torch.zeros(n, device=DEV)  # noqa: E731
+    alt = dict(master_alt=mk(), exp_avg_alt=mk(), exp_avg_sq_alt=mk()) if pipeline == "optimistic" else {}
+    grp = zdp.Group(mk(master0), mk(), mk(), flat_param=up16(flat0, dt), **alt)
+    avg = torch.empty(n, dtype=torch.float32, device=DEV)
+    ws, st = zdp.new_workspace(1), zdp.new_state(1.0)
+    og = oracle.Group(replicas=None, grad_dt=odt, master=master0.copy(), m=np.zeros(n, np.float32),
+                      v=np.zeros(n, np.float32), param=flat0.copy(), param_dt=odt)
+    ost = oracle.State()
+    flags = []
+    for k in range(3):
+        reps = _sum_overflow_copies(n, n_d, dt, k, seed) if k == 1 else \
+            [grads16_np(n, dt, 1.0, (seed, "g", k, r)) for r in range(n_d)]
+        dreps = [up16(r, dt) for r in reps]
+        if pipeline == "checked":
+            zdp.reduce_grad_segment(dreps, avg, ws, 0, st)
+            zdp.grad_norm_overflow(None, ws, 1, st, sc)
+            grp.replicas, grp.avg = None, avg
+        else:
+            grp.replicas, grp.avg = dreps, None
+        zdp.adam_step([grp], ws, st, sc)
+        og.replicas = reps
+        oracle.step([og], pol, ost)
+        torch.cuda.synchronize()
+        s = _compare_state(f"{tag} call {k + 1}", st, ost)
+        cm, cmm, cv = zdp.current_state(grp, s)
+        _compare_group(f"{tag} call {k + 1}", cm, cmm, cv, og)
+        assert_u16_equal(down16(grp.flat_param), og.param, f"{tag} call {k + 1} param")
+        flags.append(s["overflow"])
+    # the pages' overflow check on the averaged shard: only the bf16 sum overflows
+    assert flags == ([0, 1, 0] if dt == "bf16" else [0, 0, 0])
+    if dt == "bf16":
+        assert ost.step == (2 if dynamic else 3)
+        if not dynamic:
+            assert np.isnan(og.master[n // 3]) or np.isinf(og.master[n // 3])

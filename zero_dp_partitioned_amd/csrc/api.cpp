@@ -14,6 +14,10 @@
 
 using namespace zdp;
 
+namespace zdp {
+std::atomic<int32_t> g_grid_limit{0};
+}  // namespace zdp
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -64,22 +68,36 @@ class HeadCheck {
   int64_t h_ = kUnset;
 };
 
-// The device must be gfx950; checked once per device.
-int check_device() {
+// What the launches need to know of a device, found once per device.
+struct DeviceInfo {
+  bool gfx950;
+  size_t batch_lds;  // dynamic LDS per block of the batched update schedule
+};
+
+// The current device must be gfx950. *info (optional) receives its DeviceInfo.
+int check_device(DeviceInfo* info = nullptr) {
   static std::mutex mu;
-  static std::unordered_map<int, int> ok;
+  static std::unordered_map<int, DeviceInfo> known;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   std::lock_guard<std::mutex> lk(mu);
-  auto it = ok.find(dev);
-  if (it == ok.end()) {
+  auto it = known.find(dev);
+  if (it == known.end()) {
     hipDeviceProp_t prop;
     e = hipGetDeviceProperties(&prop, dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
-    it = ok.emplace(dev, strncmp(prop.gcnArchName, "gfx950", 6) == 0).first;
+    int lds = 0;
+    e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(LDS per CU)");
+    DeviceInfo d;
+    d.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.batch_lds = batch_lds_bytes(static_cast<size_t>(lds));
+    it = known.emplace(dev, d).first;
   }
-  if (!it->second) return fail(ZERO_ERR_UNSUPPORTED, "device %d is not gfx950, the target this library is built for", dev);
+  if (!it->second.gfx950)
+    return fail(ZERO_ERR_UNSUPPORTED, "device %d is not gfx950, the target this library is built for", dev);
+  if (info) *info = it->second;
   return ZERO_OK;
 }
 
@@ -381,8 +399,8 @@ int zero_grad_norm_overflow(const void* const* grads, const int64_t* counts, int
     // 16-byte-aligned copies take the wide-load scan; others the streaming pass
     const bool wide = aligned(grads[g], 16);
     if (wide) R[g].head = 0;
-    int blocks = scan_grid(R[g].n);
-    hipError_t e = wide ? launch_scan(R[g], src, s) : launch_reduce(R[g], src, vec[g], s, &blocks);
+    int blocks = 0;
+    hipError_t e = wide ? launch_scan(R[g], src, s, &blocks) : launch_reduce(R[g], src, vec[g], s, &blocks);
     if (e != hipSuccess) return hip_fail(e, "scan launch");
     e = fold_into(workspace, g, blocks, s);
     if (e != hipSuccess) return hip_fail(e, "fold launch");
@@ -487,11 +505,12 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_policy
     a.partials = checked ? nullptr : scratch_of(workspace);
     vec[g] = v;
   }
-  if (int rc = check_device()) return rc;
+  DeviceInfo dev;
+  if (int rc = check_device(&dev)) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   for (int32_t g = 0; g < n_groups; ++g) {
     int blocks = 0;
-    hipError_t e = launch_adam(A[g], src[g], vec[g], mode, s, &blocks);
+    hipError_t e = launch_adam(A[g], src[g], vec[g], mode, dev.batch_lds, s, &blocks);
     if (e != hipSuccess) return hip_fail(e, "update launch");
     if (!checked) {
       e = fold_into(workspace, g, blocks, s);
@@ -544,7 +563,7 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_policy
         AdamArgs a = A[g];
         a.partials = nullptr;
         int blocks = 0;
-        e = launch_adam(a, src[g], vec[g], kRedo, s, &blocks);
+        e = launch_adam(a, src[g], vec[g], kRedo, dev.batch_lds, s, &blocks);
         if (e != hipSuccess) return hip_fail(e, "second-pass launch");
       }
       CommitArgs C;
@@ -580,6 +599,12 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_policy
   }
   hipError_t e = launch_commit(C, s);
   return e == hipSuccess ? ZERO_OK : hip_fail(e, "commit launch");
+}
+
+int zero_set_grid_limit(int32_t max_blocks) {
+  if (max_blocks < 0) return fail(ZERO_ERR_INVALID_ARG, "max_blocks = %d < 0", max_blocks);
+  g_grid_limit.store(max_blocks, std::memory_order_relaxed);
+  return ZERO_OK;
 }
 
 int zero_cast_writeback(const float* master, int64_t n, void* flat_param, int64_t offset, int32_t param_dt,

@@ -309,9 +309,18 @@ __device__ __forceinline__ void write_block_partial(double s, int bad, double* o
 //     state->redo; as kOptimistic with the clip multiplier, no partials.
 // VEC: fp32 arrays 16-byte and 16-bit copies 8-byte aligned (quad path).
 // QL: quads per lane, so tiles of kBlock * QL * 4 elements (see tile_quads).
+// BATCH (several copies, 4-quad tiles): a full tile is read in one batch --
+//   the state of all four quads first, then every copy -- then updated, then
+//   stored one array at a time (master, m, v, parameters), each store a 1 KiB
+//   run per wave. Launched with at most two blocks per CU (see adam_launch).
+//   On the 13B shard at N_d = 8 (optimistic) this moves the step from 79.2 %
+//   to 80.0 % of 8 TB/s; either change alone, or the batch at three blocks per
+//   CU (its register-bound residency), is slower than the plain schedule.
+//   Results are the same bits: the same operations per element, and the norm
+//   partials accumulate in the same order.
 // ------------------------------------------------------------------------
 
-template <int SRC, bool VEC, int MODE, int QL>
+template <int SRC, bool VEC, int MODE, int QL, bool BATCH>
 __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs A) {
   constexpr bool CHECKED = MODE == kChecked;
   constexpr bool REDO = MODE == kRedo;
@@ -390,6 +399,52 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs A) {
   if (blockIdx.x == 0 && threadIdx.x < h) one(threadIdx.x);
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int64_t t0 = h + t * T;
+    if constexpr (BATCH && VEC && SRC != kSrcAvg && QL == kQuadsPerThread) {
+      if (A.src.n_d > 1 && t0 + T <= n) {
+        const int64_t lane4 = static_cast<int64_t>(threadIdx.x) * 4;
+        f4 T4[QL], M4[QL], V4[QL];
+#pragma unroll
+        for (int k = 0; k < QL; ++k) {
+          const int64_t e = t0 + k * kBlock * 4 + lane4;
+          T4[k] = ld_stream(reinterpret_cast<const f4*>(mst_in + e));
+          M4[k] = ld_stream(reinterpret_cast<const f4*>(m_in + e));
+          V4[k] = ld_stream(reinterpret_cast<const f4*>(v_in + e));
+        }
+        float at[QL][4];
+        source_tile<SRC, QL, 0>(A.src, t0, at);
+#pragma unroll
+        for (int k = 0; k < QL; ++k) {
+          float th[4] = {T4[k].x, T4[k].y, T4[k].z, T4[k].w};
+          float mm[4] = {M4[k].x, M4[k].y, M4[k].z, M4[k].w};
+          float vv[4] = {V4[k].x, V4[k].y, V4[k].z, V4[k].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float g = at[k][q] * s.inv_scale;
+            if constexpr (!CLIPPED) account(at[k][q], g, sumsq, bad);
+            if constexpr (CLIPPED) g = g * s.clip;
+            adam1(g, th[q], mm[q], vv[q], s);
+          }
+          T4[k] = (f4){th[0], th[1], th[2], th[3]};
+          M4[k] = (f4){mm[0], mm[1], mm[2], mm[3]};
+          V4[k] = (f4){vv[0], vv[1], vv[2], vv[3]};
+        }
+#pragma unroll
+        for (int k = 0; k < QL; ++k) st_stream(reinterpret_cast<f4*>(mst_out + t0 + k * kBlock * 4 + lane4), T4[k]);
+#pragma unroll
+        for (int k = 0; k < QL; ++k) st_stream(reinterpret_cast<f4*>(m_out + t0 + k * kBlock * 4 + lane4), M4[k]);
+#pragma unroll
+        for (int k = 0; k < QL; ++k) st_stream(reinterpret_cast<f4*>(v_out + t0 + k * kBlock * 4 + lane4), V4[k]);
+        if (pdt) {
+#pragma unroll
+          for (int k = 0; k < QL; ++k) {
+            const uint32_t hq[4] = {encode16(T4[k].x, pdt), encode16(T4[k].y, pdt), encode16(T4[k].z, pdt),
+                                    encode16(T4[k].w, pdt)};
+            store4_16(param + t0 + k * kBlock * 4 + lane4, hq, A.param_align);
+          }
+        }
+        continue;
+      }
+    }
     if constexpr (VEC && SRC != kSrcAvg) {
       // several copies, a full tile: read them copy by copy
       if (A.src.n_d > 1 && t0 + T <= n) {
@@ -712,12 +767,21 @@ __global__ void __launch_bounds__(kBlock) restore_kernel(const RestoreArgs R) {
   }
 }
 
+// The batched schedule (2 to 31 copies, 4-quad tiles) gets `batch_lds` bytes
+// of dynamic LDS per block, which it never touches: it caps the blocks
+// resident per CU at kBatchBlocksPerCU.
 template <int SRC, bool VEC, int MODE, int QL>
-hipError_t adam_launch(const AdamArgs& a, hipStream_t s, int* blocks) {
+hipError_t adam_launch(const AdamArgs& a, size_t batch_lds, hipStream_t s, int* blocks) {
   int grid = stream_grid(a.n - a.head, QL);
   if (MODE == kRedo && grid > kRedoGrid) grid = kRedoGrid;
   *blocks = grid;
-  hipLaunchKernelGGL((adam_kernel<SRC, VEC, MODE, QL>), dim3(grid), dim3(kBlock), 0, s, a);
+  if constexpr (QL == kQuadsPerThread && VEC && SRC != kSrcAvg) {
+    if (batched(SRC, VEC, a.src.n_d)) {
+      hipLaunchKernelGGL((adam_kernel<SRC, VEC, MODE, QL, true>), dim3(grid), dim3(kBlock), batch_lds, s, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((adam_kernel<SRC, VEC, MODE, QL, false>), dim3(grid), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
@@ -730,15 +794,16 @@ hipError_t reduce_launch(const ReduceArgs& a, hipStream_t s, int* blocks) {
 
 }  // namespace
 
-hipError_t launch_adam(const AdamArgs& a, int src, bool vec, int mode, hipStream_t s, int* blocks) {
+hipError_t launch_adam(const AdamArgs& a, int src, bool vec, int mode, size_t batch_lds, hipStream_t s,
+                       int* blocks) {
   const bool wide = tile_quads(src, vec, a.src.n_d) == kQuadsWide;
-#define ZDP_ADAM_MODE(SRC, VEC, QL)                                                 \
-  switch (mode) {                                                                   \
-    case kFused: return adam_launch<SRC, VEC, kFused, QL>(a, s, blocks);            \
-    case kChecked: return adam_launch<SRC, VEC, kChecked, QL>(a, s, blocks);        \
-    case kOptimistic: return adam_launch<SRC, VEC, kOptimistic, QL>(a, s, blocks);  \
-    case kRedo: return adam_launch<SRC, VEC, kRedo, QL>(a, s, blocks);              \
-    default: return hipErrorInvalidValue;                                           \
+#define ZDP_ADAM_MODE(SRC, VEC, QL)                                                            \
+  switch (mode) {                                                                              \
+    case kFused: return adam_launch<SRC, VEC, kFused, QL>(a, batch_lds, s, blocks);            \
+    case kChecked: return adam_launch<SRC, VEC, kChecked, QL>(a, batch_lds, s, blocks);        \
+    case kOptimistic: return adam_launch<SRC, VEC, kOptimistic, QL>(a, batch_lds, s, blocks);  \
+    case kRedo: return adam_launch<SRC, VEC, kRedo, QL>(a, batch_lds, s, blocks);              \
+    default: return hipErrorInvalidValue;                                                      \
   }
 #define ZDP_ADAM(SRC)                                                               \
   if (src == SRC) {                                                                 \
@@ -762,7 +827,7 @@ hipError_t launch_adam(const AdamArgs& a, int src, bool vec, int mode, hipStream
 }
 
 hipError_t launch_restore(const RestoreArgs& a, bool vec, hipStream_t s) {
-  int grid = stream_grid(a.n);
+  int grid = stream_grid(a.n);  // already within the grid limit
   if (grid > kRestoreGrid) grid = kRestoreGrid;
   if (vec)
     hipLaunchKernelGGL(restore_kernel<true>, dim3(grid), dim3(kBlock), 0, s, a);
@@ -792,8 +857,9 @@ int scan_grid(int64_t n) {
   return g < kScanGrid ? g : kScanGrid;
 }
 
-hipError_t launch_scan(const ReduceArgs& a, int src, hipStream_t s) {
-  const dim3 grid(scan_grid(a.n));
+hipError_t launch_scan(const ReduceArgs& a, int src, hipStream_t s, int* blocks) {
+  *blocks = scan_grid(a.n);
+  const dim3 grid(*blocks);
   if (src == kSrcF16) hipLaunchKernelGGL(scan_kernel<kSrcF16>, grid, dim3(kBlock), 0, s, a);
   else if (src == kSrcBF16) hipLaunchKernelGGL(scan_kernel<kSrcBF16>, grid, dim3(kBlock), 0, s, a);
   else return hipErrorInvalidValue;

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/zero_dp.h"
 
 namespace zdp {
@@ -29,6 +31,12 @@ constexpr int tile_inflight(int quads) { return quads == kQuadsWide ? kWideInfli
 // kCappedReduceCopies copies up its waves also keep at most kWideInflight
 // gradient loads in flight (1-4 % faster there, no gain with fewer copies).
 constexpr int kCappedReduceCopies = 8;
+// With 2 to kWideCopies - 1 copies the update kernel takes the batched
+// schedule (see adam_kernel): every load of a tile in flight at once, then the
+// arithmetic, then the stores array by array, with at most kBatchBlocksPerCU
+// blocks resident per compute unit. Residency is capped by giving each block
+// an otherwise unused share of the CU's LDS (batch_lds_bytes).
+constexpr int kBatchBlocksPerCU = 2;
 constexpr int kMaxGrid = 1 << 20;                    // blocks per launch (tiles beyond: grid-stride)
 constexpr int kInlineReplicas = 64;                  // replica pointers carried in the kernel arguments
 
@@ -150,21 +158,47 @@ inline int tile_quads(int src_kind, bool vec, int n_d) {
   return vec && src_kind != kSrcAvg && n_d >= kWideCopies ? kQuadsWide : kQuadsPerThread;
 }
 
+// Upper bound on the blocks of every streaming launch set by
+// zero_set_grid_limit (0: none beyond each launch's own cap). Tests lower it
+// so that small shards run the grid-stride loops of every kernel.
+extern std::atomic<int32_t> g_grid_limit;
+
+// `grid` blocks, or fewer if zero_set_grid_limit asked for fewer.
+inline int limit_grid(int grid) {
+  const int32_t lim = g_grid_limit.load(std::memory_order_relaxed);
+  return lim > 0 && lim < grid ? lim : grid;
+}
+
 // Blocks of a streaming launch over n elements (tiles of kBlock * quads * 4).
 inline int stream_grid(int64_t n, int quads = kQuadsPerThread) {
   const int64_t tile = static_cast<int64_t>(kBlock) * quads * 4;
   int64_t tiles = (n + tile - 1) / tile;
   if (tiles < 1) tiles = 1;
-  return static_cast<int>(tiles < kMaxGrid ? tiles : kMaxGrid);
+  return limit_grid(static_cast<int>(tiles < kMaxGrid ? tiles : kMaxGrid));
 }
 
 // Launchers (kernels.hip). Each returns the hipError_t of its launches.
 // `vec` selects the aligned quad path; *blocks receives the grid size, which is
 // the number of block partials the launch writes.
-hipError_t launch_adam(const AdamArgs& a, int src_kind, bool vec, int mode, hipStream_t s, int* blocks);
+// batch_lds: dynamic LDS bytes per block of the batched schedule's launches,
+// which caps them at kBatchBlocksPerCU blocks per CU on the current device.
+hipError_t launch_adam(const AdamArgs& a, int src_kind, bool vec, int mode, size_t batch_lds, hipStream_t s,
+                       int* blocks);
+// Whether an update launch takes the batched schedule.
+inline bool batched(int src_kind, bool vec, int n_d) {
+  return vec && src_kind != kSrcAvg && n_d > 1 && n_d < kWideCopies;
+}
+// LDS per block that leaves room for exactly kBatchBlocksPerCU blocks on a CU
+// with lds_per_cu bytes (each block also holds the kernels' few static bytes),
+// at most 64 KiB.
+inline size_t batch_lds_bytes(size_t lds_per_cu) {
+  size_t b = lds_per_cu / kBatchBlocksPerCU;
+  b = b > 1024 ? (b - 1024) / 256 * 256 : 0;
+  return b < (64u << 10) ? b : (64u << 10);
+}
 hipError_t launch_reduce(const ReduceArgs& a, int src_kind, bool vec, hipStream_t s, int* blocks);
 // Single-copy scan (partials only) of a 16-byte-aligned copy; scan_grid(n) blocks, one partial each.
-hipError_t launch_scan(const ReduceArgs& a, int src_kind, hipStream_t s);
+hipError_t launch_scan(const ReduceArgs& a, int src_kind, hipStream_t s, int* blocks);
 int scan_grid(int64_t n);
 hipError_t launch_fold(const FoldArgs& a, hipStream_t s);
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t s);
