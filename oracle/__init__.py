@@ -121,6 +121,10 @@ def lib():
         L.oracle_step_given_norm.argtypes = [ctypes.POINTER(_Group), ctypes.c_int32, ctypes.POINTER(_Policy),
                                              ctypes.POINTER(_State), ctypes.c_double, ctypes.c_int32]
         L.oracle_step_given_norm.restype = ctypes.c_int
+        L.oracle_step_from_average.argtypes = [ctypes.POINTER(_Group), ctypes.c_int32, ctypes.POINTER(_f32p),
+                                               ctypes.POINTER(_Policy), ctypes.POINTER(_State), ctypes.c_double,
+                                               ctypes.c_int32]
+        L.oracle_step_from_average.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -292,27 +296,26 @@ class Group:
     _keep: list = field(default_factory=list, repr=False)
 
 
-def step(groups, policy, state, norm2=None, flag=None):
-    """Run one full step over ``groups`` in place; updates ``state``. With
-    ``norm2`` and ``flag`` given, the groups hold a sample of a shard's
-    coordinates and these are the whole shard's norm² and overflow flag, which
-    the skip verdict and the clip multiplier then use."""
+def _groups_struct(groups, keep, with_replicas=True):
     G = (_Group * len(groups))()
-    keep = []
     for i, g in enumerate(groups):
-        reps, arr = _replica_array(g.replicas)
-        keep.append((reps, arr))
         n = g.master.size
         for a in (g.master, g.m, g.v):
             if a.dtype != np.float32 or not a.flags.c_contiguous or a.size != n:
                 raise ValueError("state arrays must be contiguous float32 of equal length")
-        for r in reps:
-            if r.size != n:
-                raise ValueError("replica length differs from shard length")
         G[i].n = n
-        G[i].n_d = len(reps)
         G[i].grad_dt = g.grad_dt
-        G[i].replicas = ctypes.cast(arr, ctypes.POINTER(_u16p))
+        if with_replicas:
+            reps, arr = _replica_array(g.replicas)
+            keep.append((reps, arr))
+            for r in reps:
+                if r.size != n:
+                    raise ValueError("replica length differs from shard length")
+            G[i].n_d = len(reps)
+            G[i].replicas = ctypes.cast(arr, ctypes.POINTER(_u16p))
+        else:
+            G[i].n_d = 0
+            G[i].replicas = None
         G[i].master = _ptr(g.master, ctypes.c_float)
         G[i].m = _ptr(g.m, ctypes.c_float)
         G[i].v = _ptr(g.v, ctypes.c_float)
@@ -326,10 +329,32 @@ def step(groups, policy, state, norm2=None, flag=None):
         G[i].param_dt = g.param_dt
         G[i].lr, G[i].beta1, G[i].beta2 = g.lr, g.beta1, g.beta2
         G[i].eps, G[i].weight_decay = g.eps, g.weight_decay
+    return G
+
+
+def _policy_state(policy, state):
     P = _Policy(int(policy.skip_on_overflow), int(policy.growth_interval),
                 policy.backoff, policy.growth, policy.min_scale, policy.max_grad_norm)
     S = _State(state.step, state.norm2, state.loss_scale, state.overflow,
                state.skipped, state.good_steps, state.clip, 0)
+    return P, S
+
+
+def _state_back(S, state):
+    state.step, state.norm2, state.loss_scale = S.step, S.norm2, S.loss_scale
+    state.overflow, state.skipped, state.good_steps = S.overflow, S.skipped, S.good_steps
+    state.clip = S.clip
+    return state
+
+
+def step(groups, policy, state, norm2=None, flag=None):
+    """Run one full step over ``groups`` in place; updates ``state``. With
+    ``norm2`` and ``flag`` given, the groups hold a sample of a shard's
+    coordinates and these are the whole shard's norm² and overflow flag, which
+    the skip verdict and the clip multiplier then use."""
+    keep = []
+    G = _groups_struct(groups, keep)
+    P, S = _policy_state(policy, state)
     if (norm2 is None) != (flag is None):
         raise ValueError("give both norm2 and flag, or neither")
     if norm2 is None:
@@ -339,7 +364,27 @@ def step(groups, policy, state, norm2=None, flag=None):
                                           ctypes.c_double(norm2), ctypes.c_int32(int(bool(flag))))
     if rc != 0:
         raise RuntimeError(f"oracle_step rc={rc}")
-    state.step, state.norm2, state.loss_scale = S.step, S.norm2, S.loss_scale
-    state.overflow, state.skipped, state.good_steps = S.overflow, S.skipped, S.good_steps
-    state.clip = S.clip
-    return state
+    return _state_back(S, state)
+
+
+def step_from_average(groups, avgs, policy, state, norm2, flag):
+    """One step over ``groups`` in place from their averaged gradients
+    ``avgs`` (float32 arrays, as ``average`` returns them; the groups'
+    ``replicas`` are not used) and the whole shard's norm² and overflow flag
+    (``norm_overflow`` over every group in order, or over a shard the groups
+    are a part of). Updates ``state``."""
+    if len(avgs) != len(groups):
+        raise ValueError("one average per group")
+    keep = []
+    G = _groups_struct(groups, keep, with_replicas=False)
+    avs = [_c(a, np.float32) for a in avgs]
+    for a, g in zip(avs, groups):
+        if a.size != g.master.size:
+            raise ValueError("average length differs from shard length")
+    arr = (_f32p * len(avs))(*[_ptr(a, ctypes.c_float) for a in avs])
+    P, S = _policy_state(policy, state)
+    rc = lib().oracle_step_from_average(G, len(groups), arr, ctypes.byref(P), ctypes.byref(S),
+                                        ctypes.c_double(norm2), ctypes.c_int32(int(bool(flag))))
+    if rc != 0:
+        raise RuntimeError(f"oracle_step_from_average rc={rc}")
+    return _state_back(S, state)

@@ -386,6 +386,48 @@ static float clip_multiplier(double norm2, double max_norm)
     return (float)(c < 1.0 ? c : 1.0);
 }
 
+/* The verdict and the update of DS12 §6, given the groups' averaged
+ * gradients avg[g] (as oracle_average computes them), the overflow flag and
+ * the squared norm of the unscaled gradient: record norm and flag, the clip
+ * multiplier; on overflow with skip, back the scale off and change nothing
+ * else; otherwise Adam on every group with the unscale multiplier 1/S of the
+ * scale in force, t + 1, and the growth bookkeeping. */
+static void apply_verdict(const oracle_group *groups, int32_t n_groups, float *const *avg,
+                          const oracle_policy *policy, oracle_state *st,
+                          double norm2, int32_t flag)
+{
+    const float inv_scale = (float)(1.0 / (double)st->loss_scale);
+    st->norm2 = norm2;
+    st->overflow = flag;
+    st->clip = clip_multiplier(norm2, policy->max_grad_norm);
+    if (flag && policy->skip_on_overflow) {
+        double s = (double)st->loss_scale * policy->backoff;
+        if (s < policy->min_scale)
+            s = policy->min_scale;
+        st->loss_scale = (float)s;
+        st->good_steps = 0;
+        st->skipped = 1;
+        return;
+    }
+    int64_t t = st->step + 1;
+    for (int32_t g = 0; g < n_groups; ++g) {
+        const oracle_group *G = &groups[g];
+        oracle_adam_update(G->n, avg[g], inv_scale, st->clip, G->master, G->m, G->v,
+                           G->param, G->param_dt, t, G->lr, G->beta1,
+                           G->beta2, G->eps, G->weight_decay);
+    }
+    st->step = t;
+    st->skipped = 0;
+    if (policy->skip_on_overflow) {
+        st->good_steps += 1;
+        if (policy->growth_interval > 0 &&
+            st->good_steps == policy->growth_interval) {
+            st->loss_scale = (float)((double)st->loss_scale * policy->growth);
+            st->good_steps = 0;
+        }
+    }
+}
+
 /* The step of DS12 §6 over `groups`. The overflow flag and the norm come from
  * these groups' averaged gradients, or, when `given` is set, are the caller's
  * (given_norm2, given_flag): the flag and norm² of a whole shard of which the
@@ -418,35 +460,7 @@ static int step_core(const oracle_group *groups, int32_t n_groups,
             norm2 = given_norm2;
             flag = given_flag;
         }
-        st->norm2 = norm2;
-        st->overflow = flag;
-        st->clip = clip_multiplier(norm2, policy->max_grad_norm);
-        if (flag && policy->skip_on_overflow) {
-            double s = (double)st->loss_scale * policy->backoff;
-            if (s < policy->min_scale)
-                s = policy->min_scale;
-            st->loss_scale = (float)s;
-            st->good_steps = 0;
-            st->skipped = 1;
-        } else {
-            int64_t t = st->step + 1;
-            for (int32_t g = 0; g < n_groups; ++g) {
-                const oracle_group *G = &groups[g];
-                oracle_adam_update(G->n, avg[g], inv_scale, st->clip, G->master, G->m, G->v,
-                                   G->param, G->param_dt, t, G->lr, G->beta1,
-                                   G->beta2, G->eps, G->weight_decay);
-            }
-            st->step = t;
-            st->skipped = 0;
-            if (policy->skip_on_overflow) {
-                st->good_steps += 1;
-                if (policy->growth_interval > 0 &&
-                    st->good_steps == policy->growth_interval) {
-                    st->loss_scale = (float)((double)st->loss_scale * policy->growth);
-                    st->good_steps = 0;
-                }
-            }
-        }
+        apply_verdict(groups, n_groups, avg, policy, st, norm2, flag);
     }
     for (int32_t g = 0; g < n_groups; ++g)
         free(avg[g]);
@@ -465,4 +479,23 @@ int oracle_step_given_norm(const oracle_group *groups, int32_t n_groups,
                            double norm2, int32_t flag)
 {
     return step_core(groups, n_groups, policy, st, 1, norm2, flag != 0);
+}
+
+/* The step from averaged gradients: avg[g] holds group g's average (the
+ * output of oracle_average on its copies; the groups' replica fields are not
+ * read), norm2 and flag the squared norm and overflow flag of the whole shard
+ * (oracle_norm_overflow over every group, in order, or over a shard of which
+ * the groups hold a part). Lets a caller average a large shard once, chunk by
+ * chunk, and then step each chunk. */
+int oracle_step_from_average(const oracle_group *groups, int32_t n_groups,
+                             float *const *avg, const oracle_policy *policy,
+                             oracle_state *st, double norm2, int32_t flag)
+{
+    if (!groups || n_groups < 1 || !avg || !policy || !st)
+        return OR_EINVAL;
+    for (int32_t g = 0; g < n_groups; ++g)
+        if (!avg[g] && groups[g].n > 0)
+            return OR_EINVAL;
+    apply_verdict(groups, n_groups, avg, policy, st, norm2, flag != 0);
+    return OR_OK;
 }

@@ -113,3 +113,63 @@ def test_sampled_step_with_the_shard_norm_equals_the_full_step(max_norm):
     assert sf.skipped == 0 and sf.step == 4
     if max_norm == 0.01:
         assert sf.clip < 1.0
+
+
+@pytest.mark.parametrize("max_norm", [0.0, 0.01])
+def test_chunked_step_from_averages_equals_the_full_step(max_norm):
+    # the full-size GPU tests' use of the oracle: average every chunk of a
+    # shard once (oracle_average), add the chunks' fp64 norm sums in chunk
+    # order, then step each chunk from its average with the whole shard's
+    # norm² and flag (oracle_step_from_average, every chunk from the same
+    # state before the call). The chunks' values equal the full step's bit
+    # for bit, and their states the full step's state; the chunked norm equals
+    # the full one within fp64 reassociation. Over calls with clipping, an
+    # overflow (skip), scale growth and two groups.
+    pol = oracle.Policy(skip_on_overflow=True, growth_interval=2, max_grad_norm=max_norm)
+    full = [_group(6001, 3, 41, wd=0.1, scale=64.0), _group(1499, 3, 42, scale=64.0)]
+    part = [oracle.Group(replicas=None, grad_dt=g.grad_dt, master=g.master.copy(), m=g.m.copy(), v=g.v.copy(),
+                         param=np.zeros(g.master.size, np.uint16), param_dt=oracle.BF16,
+                         weight_decay=g.weight_decay) for g in full]
+    for g in full:
+        g.param, g.param_dt = np.zeros(g.master.size, np.uint16), oracle.BF16
+    chunk = 1000
+    sf, sc = oracle.State(loss_scale=64.0), oracle.State(loss_scale=64.0)
+    for k in range(6):
+        for gi, g in enumerate(full):
+            g.replicas = [grads16_np(g.master.size, "bf16", sf.loss_scale, (43, k, gi, r)) for r in range(3)]
+            if k == 2 and gi == 1:
+                g.replicas[2] = g.replicas[2].copy()
+                g.replicas[2][1400] = 0xFFC0       # a NaN in the last chunk of the second group
+        oracle.step(full, pol, sf)
+        inv = oracle.inv_scale_of(sc.loss_scale)
+        chunks, n2, flag = [], 0.0, 0
+        for gi, g in enumerate(full):
+            for s in range(0, g.master.size, chunk):
+                e = min(g.master.size, s + chunk)
+                a = oracle.average([r[s:e] for r in g.replicas], g.grad_dt)
+                c2, cf = oracle.norm_overflow(a, inv)
+                n2, flag = n2 + c2, flag | cf
+                chunks.append((gi, s, e, a))
+        after = []
+        for gi, s, e, a in chunks:
+            p = part[gi]
+            cg = oracle.Group(replicas=None, grad_dt=p.grad_dt, master=p.master[s:e], m=p.m[s:e], v=p.v[s:e],
+                              param=p.param[s:e], param_dt=p.param_dt, weight_decay=p.weight_decay)
+            st = oracle.State(**vars(sc))
+            oracle.step_from_average([cg], [a], pol, st, n2, flag)
+            after.append(st)
+        def same(x, y):   # NaN norms compare equal
+            return all(a == b or (a != a and b != b) for a, b in zip(vars(x).values(), vars(y).values()))
+        assert all(same(st, after[0]) for st in after)
+        sc = after[0]
+        assert abs(sc.norm2 - sf.norm2) <= 1e-12 * sf.norm2 or not np.isfinite(sf.norm2)
+        assert (sc.step, sc.skipped, sc.loss_scale, sc.good_steps, sc.overflow) == \
+               (sf.step, sf.skipped, sf.loss_scale, sf.good_steps, sf.overflow)
+        assert sc.clip == sf.clip
+        for g, p in zip(full, part):
+            for a, b in ((g.master, p.master), (g.m, p.m), (g.v, p.v)):
+                np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+            np.testing.assert_array_equal(g.param, p.param)
+    assert sf.step == 5
+    if max_norm == 0.01:
+        assert sf.clip < 1.0

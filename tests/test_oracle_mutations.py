@@ -43,8 +43,10 @@ MUTATIONS = [
     ("overflow flag never set", "if (!isfinite(a[j]))\n            f = 1;", "if (0)\n            f = 1;"),
     ("skip does not lower the scale", "double s = (double)st->loss_scale * policy->backoff;",
      "double s = (double)st->loss_scale;"),
-    ("skipped step still counted", "st->good_steps = 0;\n            st->skipped = 1;",
-     "st->good_steps = 0;\n            st->skipped = 1;\n            st->step += 1;"),
+    ("skipped step still counted", "st->good_steps = 0;\n        st->skipped = 1;",
+     "st->good_steps = 0;\n        st->skipped = 1;\n        st->step += 1;"),
+    ("average-fed step ignores the shard flag", "apply_verdict(groups, n_groups, avg, policy, st, norm2, flag != 0);",
+     "apply_verdict(groups, n_groups, avg, policy, st, norm2, 0);"),
     ("skip ignored", "if (flag && policy->skip_on_overflow) {", "if (0) {"),
     ("scale never grows", "st->loss_scale = (float)((double)st->loss_scale * policy->growth);", "(void)0;"),
     ("ties rounded away from zero", "r = (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "r = fl + 1.0;"),
