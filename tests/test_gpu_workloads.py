@@ -1,18 +1,29 @@
 """The five workloads at full size, in the launch configuration bench.py times.
 
-* tiny (and its literal shape list): every element against the oracle.
-* GPT-2 1.5B, 7.5B at N_d=64, 13B at N_d=8 (dynamic loss scale with one
-  overflowing call), LLaMA-3 8B (AdamW, two groups): the elementwise outputs
-  on a fixed sample of coordinates (first and last 64, tensor and group
-  boundaries, the injected inf, 4096 random ones) stepped by the oracle from
-  the same inputs -- each coordinate's update depends only on that coordinate,
-  so a sample is checked exactly; the gradient norm and the overflow flag over
-  all elements by the oracle on the first call and on the overflowing call
-  (chunked, chunk sums added in order); the flag, skip verdict, step count and
-  loss scale on every call.
+* GPT-2 1.5B, 7.5B at N_d=64 (rank 63), 13B at N_d=8 (rank 7; dynamic loss
+  scale with one overflowing call; the checked and the optimistic pipeline on
+  the same gradient copies; with and without clipping): every element of
+  master, m, v and the parameter slice on every call, against the oracle
+  stepped chunk by chunk on the host (tests/_fullsize.py). The two 13B
+  pipelines are also compared with each other on the device.
+* LLaMA-3 8B (AdamW, two groups): every element of the norm group and of a
+  chunk sample of the matrix group on every call -- every 64th 16M-element
+  chunk, the first and the last, every chunk holding a tensor boundary, and
+  every chunk past element 2^32, where the update kernel's grid (2^20 tiles of
+  4096 elements) starts its second round; the norm and the flag over all
+  elements.
+* tiny (and its literal shape list): every element.
+* Rank 0 of the 7.5B and 13B shards (offset 0): a fixed sample of coordinates
+  (first and last 64, tensor boundaries, 4096 random ones) stepped by the
+  oracle from the same inputs, norm and flag over all elements on the first
+  call.
+On every call: the overflow flag, skip verdict, step count, loss scale and
+clip multiplier; the norm within 1e-10 relative.
 """
 import dataclasses
+import gc
 import os
+import time
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
@@ -24,7 +35,9 @@ import zero_dp_partitioned_amd as zdp
 from zero_dp_partitioned_amd import layout
 from workloads import WORKLOADS, derive_seed, fill_normal_, torch_dtype
 
+from _fullsize import FullCheck, GroupCheck, chunk_for
 from _gpu_helpers import DEV, ORACLE_DT, assert_bits_equal, assert_u16_equal, down16, down32
+from _parity import Bar
 
 pytestmark = pytest.mark.gpu
 
@@ -238,6 +251,212 @@ def _free():
     torch.cuda.empty_cache()
 
 
+SAMPLE_CHUNK = 1 << 24        # the chunk of the large-shard sample (16M elements)
+SECOND_ROUND = 4096 << 20     # elements one update launch covers before its grid loops
+
+
+def llama_sample(n, boundaries):
+    """The LLaMA-3 matrix group's checked ranges: 16M-element chunks -- every
+    64th, the first, the last, every one holding a tensor boundary, and every
+    one that reaches past element 2^32 (the second grid-stride round of the
+    update kernel) -- as sorted disjoint [(start, end)]."""
+    last = (n - 1) // SAMPLE_CHUNK
+    pick = set(range(0, last + 1, 64)) | {0, last}
+    pick |= {b // SAMPLE_CHUNK for b in boundaries if 0 <= b < n}
+    pick |= set(range(max(0, (SECOND_ROUND - 1) // SAMPLE_CHUNK), last + 1))
+    return [(c * SAMPLE_CHUNK, min(n, (c + 1) * SAMPLE_CHUNK)) for c in sorted(pick)]
+
+
+class FullRun:
+    """A workload at full size for one or two pipelines on the same gradient
+    copies (laid out as bench.py lays them out: one arena over HBM's regions,
+    copies as a pointer table), with the oracle stepping every checked
+    element on the host (tests/_fullsize.py). The last pipeline named is the
+    one compared with the oracle; the others are compared with it on the
+    device, bit for bit."""
+
+    def __init__(self, key, pipelines=("fused",), max_grad_norm=0.0, sampled=False):
+        self.wl = wl = WORKLOADS[key]
+        self.pipelines = pipelines
+        self.max_grad_norm = max_grad_norm
+        gdt, pdt = torch_dtype(wl.grad_dt), torch_dtype(wl.param_dt)
+        self.odt = ORACLE_DT[wl.grad_dt]
+        shards = []
+        for spec in wl.groups:
+            psi = sum(spec.numels)
+            segs, _ = zdp.partition(psi, wl.n_d)
+            o_off, o_size, _ = oracle.partition(psi, wl.n_d)
+            assert segs[wl.rank] == (int(o_off[wl.rank]), int(o_size[wl.rank]))
+            shards.append((psi, *segs[wl.rank]))
+        specs = []
+        for p in pipelines:
+            sp = "fused" if p == "checked" and wl.n_d == 1 else p
+            for b in layout.step_specs(shards, wl.n_d, gdt, pdt, sp, wl.n_d <= layout.INLINE_COPIES):
+                if b.key[1] == "grad":
+                    if p == pipelines[0]:
+                        specs.append(b)            # one set of copies for every pipeline
+                else:
+                    specs.append(dataclasses.replace(b, key=(p,) + b.key))
+        buf, self.placement = layout.allocate(specs, DEV, "regions")
+        print(f"  layout: {self.placement}", flush=True)
+        self.reps = []
+        self.side = {p: dict(groups=[], avg=None) for p in pipelines}
+        self.outside = []
+        for gi, (spec, (psi, off, n)) in enumerate(zip(wl.groups, shards)):
+            self.reps.append(layout.copies_of(buf, gi, wl.n_d, n))
+            for p in pipelines:
+                master = buf[(p, gi, "master")][:n]
+                fill_normal_(master, 0.02, derive_seed(wl.key, gi, "master"))
+                flat = buf[(p, gi, "flat")][:psi]
+                fill_normal_(flat, 0.02, derive_seed(wl.key, gi, "flat"))
+                flat[off:off + n].copy_(master)
+                alt = {}
+                if p == "optimistic":
+                    alt = {name: buf[(p, gi, name)][:n] for name in ("master_alt", "exp_avg_alt", "exp_avg_sq_alt")}
+                self.side[p]["groups"].append(zdp.Group(
+                    master=master, exp_avg=buf[(p, gi, "exp_avg")][:n].zero_(),
+                    exp_avg_sq=buf[(p, gi, "exp_avg_sq")][:n].zero_(), replicas=self.reps[gi], flat_param=flat,
+                    param_offset=off, lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2, eps=wl.eps,
+                    weight_decay=spec.weight_decay, **alt))
+            outs = np.unique(np.array([0, off - 1, off + n, psi - 1], dtype=np.int64))
+            outs = outs[(outs >= 0) & (outs < psi) & ((outs < off) | (outs >= off + n))]
+            flat = self.side[pipelines[-1]]["groups"][gi].flat_param
+            self.outside.append((outs, _u16(flat[torch.from_numpy(outs).to(DEV)]) if outs.size else None))
+        for p in pipelines:
+            d = self.side[p]
+            d["ws"] = zdp.new_workspace(len(wl.groups))
+            d["state"] = zdp.new_state(wl.loss_scale)
+            needs_norm = wl.dynamic_loss_scale or max_grad_norm > 0
+            d["policy"] = (zdp.policy(wl.dynamic_loss_scale, optimistic=p == "optimistic", max_grad_norm=max_grad_norm)
+                           if needs_norm else None)
+            if p == "checked" and wl.n_d > 1:
+                d["avg"] = [buf[(p, gi, "avg")][:g.master.numel()] for gi, g in enumerate(d["groups"])]
+        # the oracle's side: the last pipeline, element by element
+        main = self.side[pipelines[-1]]
+        self.last_state = {"cur": 0}
+        checks = []
+        for gi, (spec, (psi, off, n)) in enumerate(zip(wl.groups, shards)):
+            g = main["groups"][gi]
+            ranges = [(0, n)]
+            if sampled and n > SAMPLE_CHUNK:
+                bounds = [sl[1] for sl in zdp.partition_tensors(list(spec.numels), wl.n_d, wl.rank)]
+                ranges = llama_sample(n, bounds)
+
+            def state(g=g):
+                return zdp.current_state(g, self.last_state)
+            gc = GroupCheck(n, self.reps[gi], g.flat_param, off, ranges, chunk_for(wl.n_d), self.odt,
+                            ORACLE_DT[wl.param_dt], wl.lr, wl.beta1, wl.beta2, wl.eps, spec.weight_decay)
+            gc.state = state
+            checks.append(gc)
+            print(f"  group {gi}: {gc.elements()} of {n} elements checked element by element", flush=True)
+        self.check = FullCheck(checks, oracle.Policy(skip_on_overflow=wl.dynamic_loss_scale,
+                                                     max_grad_norm=max_grad_norm), wl.loss_scale)
+        self.check.load_initial()
+        self.bar = Bar(lr=wl.lr, beta1=wl.beta1)
+
+    def draw_grads(self, call):
+        wl = self.wl
+        scale = self.check.ostate.loss_scale  # the scale in force (asserted equal on every side)
+        for gi, reps in enumerate(self.reps):
+            for r, t in enumerate(reps):
+                fill_normal_(t, 1e-3, derive_seed(wl.key, gi, "grad", call, r), scale=scale)
+        if wl.inf_at is not None and wl.inf_at[0] == call:
+            _, rep, where = wl.inf_at
+            pos = self.reps[0][0].numel() // 2 if where == "mid" else int(where)
+            self.reps[0][rep][pos] = float("inf")
+            print(f"  call {call}: +inf in copy {rep} at {pos}", flush=True)
+
+    def gpu_step(self, p):
+        d = self.side[p]
+        groups, ws, st, pol = d["groups"], d["ws"], d["state"], d["policy"]
+        if pol is None or p == "optimistic":
+            zdp.adam_step(groups, ws, st, pol)
+            return
+        if self.wl.n_d == 1:
+            zdp.grad_norm_overflow([g.replicas[0] for g in groups], ws, len(groups), st, pol)
+            zdp.adam_step(groups, ws, st, pol)
+            return
+        for gi, g in enumerate(groups):
+            zdp.reduce_grad_segment(g.replicas, d["avg"][gi], ws, gi, st)
+        zdp.grad_norm_overflow(None, ws, len(groups), st, pol)
+        saved = [g.replicas for g in groups]
+        for gi, g in enumerate(groups):
+            g.replicas, g.avg = None, d["avg"][gi]
+        try:
+            zdp.adam_step(groups, ws, st, pol)
+        finally:
+            for gi, g in enumerate(groups):
+                g.replicas, g.avg = saved[gi], None
+
+    def _device_equal(self, tag, a, b, step=1 << 28):
+        """Bitwise equality of two device tensors, compared in pieces."""
+        iv = torch.int32 if a.dtype == torch.float32 else torch.int16
+        av, bv = a.view(iv), b.view(iv)
+        for s in range(0, av.numel(), step):
+            x, y = av[s:s + step], bv[s:s + step]
+            if not torch.equal(x, y):
+                i = int(torch.nonzero(x != y)[0])
+                raise AssertionError(f"{tag}: pipelines differ at element {s + i}: {int(x[i])} vs {int(y[i])}")
+
+    def run(self, steps=None):
+        wl = self.wl
+        steps = wl.steps if steps is None else steps
+        main = self.pipelines[-1]
+        for call in range(1, steps + 1):
+            t0 = time.perf_counter()
+            self.draw_grads(call)
+            for p in self.pipelines:
+                self.gpu_step(p)
+            torch.cuda.synchronize()
+            states = {p: zdp.read_state(self.side[p]["state"]) for p in self.pipelines}
+            s = states[main]
+            tag = f"{wl.key} call {call}"
+            for p in self.pipelines[:-1]:
+                o = states[p]
+                for k in ("step", "skipped", "overflow", "loss_scale", "good_steps", "clip_coef"):
+                    assert o[k] == s[k], (tag, p, k, o[k], s[k])
+                for gi, (ga, gb) in enumerate(zip(self.side[p]["groups"], self.side[main]["groups"])):
+                    for name, x, y in zip(("master", "exp_avg", "exp_avg_sq"), zdp.current_state(ga, o),
+                                          zdp.current_state(gb, s)):
+                        self._device_equal(f"{tag} group {gi} {name} ({p} vs {main})", x, y)
+                    n, off = ga.master.numel(), ga.param_offset
+                    self._device_equal(f"{tag} group {gi} param ({p} vs {main})", ga.flat_param[off:off + n],
+                                       gb.flat_param[off:off + n])
+            t1 = time.perf_counter()
+            self.last_state = s
+            ost = self.check.step_and_compare(tag, self.bar, s)
+            assert s["step"] == ost.step, tag
+            assert s["skipped"] == ost.skipped, tag
+            assert s["overflow"] == ost.overflow, tag
+            assert s["loss_scale"] == np.float32(ost.loss_scale), tag
+            assert s["good_steps"] == ost.good_steps, tag
+            assert s["redo"] == 0, tag
+            if np.isfinite(ost.norm2):
+                assert abs(s["grad_norm_sq"] - ost.norm2) <= 1e-10 * ost.norm2, (tag, s["grad_norm_sq"], ost.norm2)
+                assert s["grad_norm"] == pytest.approx(np.sqrt(ost.norm2), rel=1e-6)
+            else:
+                assert not np.isfinite(s["grad_norm_sq"]), tag
+            print(f"  {tag}: ok (step {s['step']}, norm {s['grad_norm']:.6g}, scale {s['loss_scale']}, "
+                  f"skipped {s['skipped']}, clip {s['clip_coef']:.6g}, exact {self.bar.exact}; device "
+                  f"{t1 - t0:.1f} s, oracle {time.perf_counter() - t1:.1f} s)", flush=True)
+        for gi, (outs, before) in enumerate(self.outside):
+            if before is not None:
+                flat = self.side[main]["groups"][gi].flat_param
+                assert_u16_equal(_u16(flat[torch.from_numpy(outs).to(DEV)]), before,
+                                 wl.key + " flat vector outside the shard")
+        return self.check.ostate
+
+    def close(self):
+        self.check.close()
+
+
+def _done(run):
+    run.close()
+    del run
+    gc.collect()
+    _free()
+
+
 @pytest.mark.parametrize("key", ["tiny", "tiny_literal"])
 def test_tiny_every_element(key):
     print(f"[workload] {key}", flush=True)
@@ -246,20 +465,22 @@ def test_tiny_every_element(key):
     _free()
 
 
-@pytest.mark.timeout(600)
-def test_gpt2_1_5b():
+@pytest.mark.timeout(900)
+def test_gpt2_1_5b_every_element():
     print("[workload] gpt2_1.5b", flush=True)
-    st = Run("gpt2_1.5b").run(full_scan_calls=(1,))
+    run = FullRun("gpt2_1.5b")
+    st = run.run()
     assert st.step == 10 and st.loss_scale == 65536.0
-    _free()
+    _done(run)
 
 
-@pytest.mark.timeout(600)
-def test_7_5b_nd64():
+@pytest.mark.timeout(900)
+def test_7_5b_nd64_every_element():
     print("[workload] 7.5b_nd64", flush=True)
-    st = Run("7.5b_nd64").run(full_scan_calls=(1,))
+    run = FullRun("7.5b_nd64")
+    st = run.run()
     assert st.step == 10
-    _free()
+    _done(run)
 
 
 @pytest.mark.timeout(900)
@@ -279,45 +500,44 @@ def test_13b_nd8_rank0():
     _free()
 
 
-@pytest.mark.timeout(900)
-@pytest.mark.parametrize("pipeline", ["checked", "optimistic"])
-def test_13b_nd8_overflow_skip(pipeline):
-    print(f"[workload] 13b_nd8 ({pipeline})", flush=True)
-    st = Run("13b_nd8", optimistic=pipeline == "optimistic").run(full_scan_calls=(1,))
-    # ten calls, the fourth overflows: nine applied steps, scale halved once
+@pytest.mark.timeout(1200)
+def test_13b_nd8_overflow_skip_every_element():
+    # both dynamic-scale pipelines on the same copies: ten calls, the fourth overflows:
+    # nine applied steps, the scale halved once
+    print("[workload] 13b_nd8 (checked and optimistic)", flush=True)
+    run = FullRun("13b_nd8", pipelines=("checked", "optimistic"))
+    st = run.run()
     assert st.step == 9 and st.loss_scale == 32768.0
-    _free()
+    _done(run)
 
 
 @pytest.mark.timeout(900)
-def test_gpt2_1_5b_clipping():
+def test_gpt2_1_5b_clipping_every_element():
     # clipping on the single-copy shard (the norm is about 39, the threshold 1): the checked pipeline
     # scans the copy first (the wide-load scan loops its capped grid over 380,277 tiles), then updates
     print("[workload] gpt2_1.5b clipping", flush=True)
-    run = Run("gpt2_1.5b", max_grad_norm=1.0)
+    run = FullRun("gpt2_1.5b", pipelines=("checked",), max_grad_norm=1.0)
     st = run.run(steps=3)
     assert st.step == 3 and st.clip < 1.0
-    del run
-    _free()
+    _done(run)
 
 
-@pytest.mark.timeout(900)
-@pytest.mark.parametrize("pipeline", ["checked", "optimistic"])
-def test_13b_nd8_clipping(pipeline):
-    # clipping at full size (the norm is about 14, the threshold 10: every applied call clips),
-    # five calls with the overflow on the fourth; the optimistic pipeline's second pass loops over
-    # the shard's 396,729 tiles with its capped grid
-    print(f"[workload] 13b_nd8 clipping ({pipeline})", flush=True)
-    run = Run("13b_nd8", optimistic=pipeline == "optimistic", max_grad_norm=10.0)
+@pytest.mark.timeout(1200)
+def test_13b_nd8_clipping_every_element():
+    # clipping at full size (the norm is about 14, the threshold 10: every applied call clips), five
+    # calls with the overflow on the fourth, both dynamic-scale pipelines on the same copies; the
+    # optimistic pipeline's second pass loops over the shard's 396,729 tiles with its capped grid
+    print("[workload] 13b_nd8 clipping (checked and optimistic)", flush=True)
+    run = FullRun("13b_nd8", pipelines=("checked", "optimistic"), max_grad_norm=10.0)
     st = run.run(steps=5)
     assert st.step == 4 and st.loss_scale == 32768.0 and st.clip < 1.0
-    del run
-    _free()
+    _done(run)
 
 
-@pytest.mark.timeout(900)
-def test_llama3_8b_adamw_two_groups():
+@pytest.mark.timeout(1200)
+def test_llama3_8b_adamw_two_groups_chunk_sample():
     print("[workload] llama3_8b", flush=True)
-    st = Run("llama3_8b").run(full_scan_calls=(1,))
+    run = FullRun("llama3_8b", sampled=True)
+    st = run.run()
     assert st.step == 5
-    _free()
+    _done(run)
