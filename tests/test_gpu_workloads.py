@@ -276,6 +276,8 @@ class FullRun:
     device, bit for bit."""
 
     def __init__(self, key, pipelines=("fused",), max_grad_norm=0.0, sampled=False):
+        gc.collect()          # a previous run's arena must be gone before this one takes all free memory
+        torch.cuda.empty_cache()
         self.wl = wl = WORKLOADS[key]
         self.pipelines = pipelines
         self.max_grad_norm = max_grad_norm
@@ -344,11 +346,11 @@ class FullRun:
 
             def state(g=g):
                 return zdp.current_state(g, self.last_state)
-            gc = GroupCheck(n, self.reps[gi], g.flat_param, off, ranges, chunk_for(wl.n_d), self.odt,
-                            ORACLE_DT[wl.param_dt], wl.lr, wl.beta1, wl.beta2, wl.eps, spec.weight_decay)
-            gc.state = state
-            checks.append(gc)
-            print(f"  group {gi}: {gc.elements()} of {n} elements checked element by element", flush=True)
+            chk = GroupCheck(n, self.reps[gi], g.flat_param, off, ranges, chunk_for(wl.n_d), self.odt,
+                             ORACLE_DT[wl.param_dt], wl.lr, wl.beta1, wl.beta2, wl.eps, spec.weight_decay)
+            chk.state = state
+            checks.append(chk)
+            print(f"  group {gi}: {chk.elements()} of {n} elements checked element by element", flush=True)
         self.check = FullCheck(checks, oracle.Policy(skip_on_overflow=wl.dynamic_loss_scale,
                                                      max_grad_norm=max_grad_norm), wl.loss_scale)
         self.check.load_initial()
@@ -447,7 +449,14 @@ class FullRun:
         return self.check.ostate
 
     def close(self):
+        """Shut the oracle's pool and drop every reference to device memory
+        (the state functions refer back to the run)."""
         self.check.close()
+        for g in self.check.groups:
+            g.state = g.reps = g.flat = None
+            g.host.clear()
+        self.check.groups = []
+        self.side = self.reps = self.outside = None
 
 
 def _done(run):
