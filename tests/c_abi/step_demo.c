@@ -5,15 +5,26 @@
  * `n_d` over a flat fp16 vector of `psi` elements), places its buffers in one
  * hipMalloc'd arena at the offsets zero_plan_arena gives (64 MiB regions, so
  * the arena stays small), fills the inputs from a fixed integer recipe, runs
- * `steps` fused steps on the null stream, and writes the inputs and results
- * to a binary file for the test to check against the CPU oracle:
+ * `steps` steps on the null stream, and writes the inputs and results to a
+ * binary file for the test to check against the CPU oracle:
  *
- *   step_demo OUT PSI N_D RANK STEPS
+ *   step_demo OUT PSI N_D RANK STEPS [checked]
  *
- * File layout (little endian): int64 psi, n_d, rank, offset, size, steps;
- * uint16 replicas[steps][n_d][size]; float master0[size];
- * float master[size], m[size], v[size]; uint16 flat[psi] (after);
- * uint16 flat0[psi] (before); double grad_norm_sq; int64 step.
+ * Default: the fused pipeline (zero_adam_step on the copies, static loss
+ * scale 1). "checked": the verdict before the update, with a dynamic loss
+ * scale starting at 1024 -- zero_reduce_grad_segment averages the copies into
+ * an fp32 buffer, zero_grad_norm_overflow forms the norm and the skip verdict,
+ * zero_adam_step updates from the average; the second step has +inf written
+ * into the last copy at element size / 2, so it is voided and the scale
+ * halves. Either way the program ends with zero_cast_writeback of the master
+ * into a bf16 copy of the flat vector at the rank's offset.
+ *
+ * File layout (little endian): int64 psi, n_d, rank, offset, size, steps,
+ * checked; uint16 replicas[steps][n_d][size] (as stepped, the inf included);
+ * float master0[size]; float master[size], m[size], v[size]; uint16 flat[psi]
+ * (after); uint16 flat0[psi] (before); uint16 cast[psi] (the bf16 vector
+ * after the cast; before it, flat0's bits); double grad_norm_sq; int64 step;
+ * float loss_scale; int32 overflow, skipped.
  */
 #include <stdint.h>
 #include <stdio.h>
@@ -62,8 +73,13 @@ static uint16_t grad_bits(uint64_t key) {
 }
 
 int main(int argc, char** argv) {
-  if (argc != 6) {
-    fprintf(stderr, "usage: %s OUT PSI N_D RANK STEPS\n", argv[0]);
+  if (argc != 6 && argc != 7) {
+    fprintf(stderr, "usage: %s OUT PSI N_D RANK STEPS [checked]\n", argv[0]);
+    return 1;
+  }
+  const int checked = argc == 7 && strcmp(argv[6], "checked") == 0;
+  if (argc == 7 && !checked) {
+    fprintf(stderr, "bad arguments\n");
     return 1;
   }
   const char* out_path = argv[1];
@@ -91,19 +107,22 @@ int main(int argc, char** argv) {
     for (int32_t r = 0; r < n_d; ++r)
       for (int64_t j = 0; j < n; ++j)
         reps[(k * n_d + r) * n + j] = grad_bits(((uint64_t)k << 48) ^ ((uint64_t)r << 40) ^ (uint64_t)(off + j));
+  if (checked && steps >= 2) reps[(1 * n_d + (n_d - 1)) * n + n / 2] = 0x7C00; /* +inf: the second step overflows */
 
-  /* device buffers, owned here: master, m, v, the n_d copies (one buffer) and
-   * the flat vector, carved from one arena */
-  zero_arena_buffer plan[5];
+  /* device buffers, owned here: master, m, v, the n_d copies (one buffer),
+   * the flat vector, the fp32 average (checked pipeline) and the bf16 copy of
+   * the flat vector the final cast writes into, carved from one arena */
+  enum { NB = 7 };
+  zero_arena_buffer plan[NB];
   memset(plan, 0, sizeof plan);
-  const int64_t sizes[5] = {4 * n, 4 * n, 4 * n, 2 * n * n_d, 2 * psi};
-  const int64_t traffic[5] = {8 * n, 8 * n, 8 * n, 2 * n * n_d, 2 * n};
-  for (int i = 0; i < 5; ++i) {
+  const int64_t sizes[NB] = {4 * n, 4 * n, 4 * n, 2 * n * n_d, 2 * psi, 4 * n, 2 * psi};
+  const int64_t traffic[NB] = {8 * n, 8 * n, 8 * n, 2 * n * n_d, 2 * n, 8 * n, 2 * n};
+  for (int i = 0; i < NB; ++i) {
     plan[i].bytes = sizes[i] > 0 ? sizes[i] : 1;
     plan[i].traffic = traffic[i];
   }
   int64_t arena_bytes = 0;
-  ZERO_OK_OR_DIE(zero_plan_arena(plan, 5, 64LL << 20, 0, 1LL << 30, &arena_bytes));
+  ZERO_OK_OR_DIE(zero_plan_arena(plan, NB, 64LL << 20, 0, 1LL << 30, &arena_bytes));
   char* d_arena;
   HIP_OK(hipMalloc((void**)&d_arena, (size_t)arena_bytes));
   float* d_master = (float*)(d_arena + plan[0].offset);
@@ -111,6 +130,8 @@ int main(int argc, char** argv) {
   float* d_v = (float*)(d_arena + plan[2].offset);
   uint16_t* d_reps = (uint16_t*)(d_arena + plan[3].offset);
   uint16_t* d_flat = (uint16_t*)(d_arena + plan[4].offset);
+  float* d_avg = (float*)(d_arena + plan[5].offset);
+  uint16_t* d_cast = (uint16_t*)(d_arena + plan[6].offset);
   void *d_ws, *d_state;
   const size_t ws_bytes = zero_workspace_bytes(1);
   HIP_OK(hipMalloc(&d_ws, ws_bytes));
@@ -119,7 +140,15 @@ int main(int argc, char** argv) {
   HIP_OK(hipMemset(d_m, 0, sizeof(float) * (size_t)n));
   HIP_OK(hipMemset(d_v, 0, sizeof(float) * (size_t)n));
   HIP_OK(hipMemcpy(d_flat, flat0, sizeof(uint16_t) * (size_t)psi, hipMemcpyHostToDevice));
-  ZERO_OK_OR_DIE(zero_state_init((zero_step_state*)d_state, 1.0f, NULL));
+  HIP_OK(hipMemcpy(d_cast, flat0, sizeof(uint16_t) * (size_t)psi, hipMemcpyHostToDevice));
+  ZERO_OK_OR_DIE(zero_state_init((zero_step_state*)d_state, checked ? 1024.0f : 1.0f, NULL));
+  zero_policy policy;
+  memset(&policy, 0, sizeof policy);
+  policy.skip_on_overflow = 1;
+  policy.growth_interval = 1000;
+  policy.backoff = 0.5;
+  policy.growth = 2.0;
+  policy.min_scale = 1.0;
 
   const void* rep_ptrs[64];
   for (int32_t r = 0; r < n_d; ++r) rep_ptrs[r] = d_reps + (size_t)r * (size_t)n;
@@ -140,26 +169,44 @@ int main(int argc, char** argv) {
   g.beta2 = 0.999;
   g.eps = 1e-8;
   g.weight_decay = 0.01;
+  zero_step_state* st_dev = (zero_step_state*)d_state;
   for (int64_t k = 0; k < steps; ++k) {
     HIP_OK(hipMemcpy(d_reps, reps + k * n_d * n, sizeof(uint16_t) * (size_t)(n_d * n), hipMemcpyHostToDevice));
-    ZERO_OK_OR_DIE(zero_adam_step(&g, 1, NULL, d_ws, ws_bytes, (zero_step_state*)d_state, NULL));
+    if (!checked) {
+      ZERO_OK_OR_DIE(zero_adam_step(&g, 1, NULL, d_ws, ws_bytes, st_dev, NULL));
+      continue;
+    }
+    /* the verdict first: average, norm and flag, then the update from the average */
+    ZERO_OK_OR_DIE(zero_reduce_grad_segment(rep_ptrs, n_d, ZERO_DT_F16, n, d_avg, d_ws, ws_bytes, 0, st_dev, NULL));
+    ZERO_OK_OR_DIE(zero_grad_norm_overflow(NULL, NULL, ZERO_DT_F16, 1, d_ws, ws_bytes, &policy, st_dev, NULL));
+    g.replicas = NULL;
+    g.n_d = 0;
+    g.avg = d_avg;
+    ZERO_OK_OR_DIE(zero_adam_step(&g, 1, &policy, d_ws, ws_bytes, st_dev, NULL));
+    g.replicas = rep_ptrs;
+    g.n_d = n_d;
+    g.avg = NULL;
   }
+  /* the master, rounded to bf16, into the other copy of the flat vector */
+  ZERO_OK_OR_DIE(zero_cast_writeback(d_master, n, d_cast, off, ZERO_DT_BF16, NULL));
   HIP_OK(hipDeviceSynchronize());
 
   float* master = malloc(sizeof(float) * (size_t)n);
   float* m = malloc(sizeof(float) * (size_t)n);
   float* v = malloc(sizeof(float) * (size_t)n);
   uint16_t* flat = malloc(sizeof(uint16_t) * (size_t)psi);
+  uint16_t* cast = malloc(sizeof(uint16_t) * (size_t)psi);
   zero_step_state st;
   HIP_OK(hipMemcpy(master, d_master, sizeof(float) * (size_t)n, hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(m, d_m, sizeof(float) * (size_t)n, hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(v, d_v, sizeof(float) * (size_t)n, hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(flat, d_flat, sizeof(uint16_t) * (size_t)psi, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(cast, d_cast, sizeof(uint16_t) * (size_t)psi, hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(&st, d_state, sizeof st, hipMemcpyDeviceToHost));
 
   FILE* f = fopen(out_path, "wb");
   if (!f) return 4;
-  const int64_t hdr[6] = {psi, n_d, rank, off, n, steps};
+  const int64_t hdr[7] = {psi, n_d, rank, off, n, steps, checked};
   fwrite(hdr, sizeof hdr, 1, f);
   fwrite(reps, sizeof(uint16_t), (size_t)(steps * n_d * n), f);
   fwrite(master0, sizeof(float), (size_t)n, f);
@@ -168,13 +215,17 @@ int main(int argc, char** argv) {
   fwrite(v, sizeof(float), (size_t)n, f);
   fwrite(flat, sizeof(uint16_t), (size_t)psi, f);
   fwrite(flat0, sizeof(uint16_t), (size_t)psi, f);
+  fwrite(cast, sizeof(uint16_t), (size_t)psi, f);
   fwrite(&st.grad_norm_sq, sizeof(double), 1, f);
   fwrite(&st.step, sizeof(int64_t), 1, f);
+  fwrite(&st.loss_scale, sizeof(float), 1, f);
+  fwrite(&st.overflow, sizeof(int32_t), 1, f);
+  fwrite(&st.skipped, sizeof(int32_t), 1, f);
   fclose(f);
-  printf("step_demo: psi=%lld n_d=%d rank=%d offset=%lld n=%lld steps=%lld norm=%g arena=%lld bytes, regions",
-         (long long)psi, n_d, rank, (long long)off, (long long)n, (long long)steps, (double)st.grad_norm,
-         (long long)arena_bytes);
-  for (int i = 0; i < 5; ++i) printf(" %d", plan[i].region);
+  printf("step_demo: %s psi=%lld n_d=%d rank=%d offset=%lld n=%lld steps=%lld norm=%g scale=%g arena=%lld bytes, "
+         "regions", checked ? "checked" : "fused", (long long)psi, n_d, rank, (long long)off, (long long)n,
+         (long long)steps, (double)st.grad_norm, (double)st.loss_scale, (long long)arena_bytes);
+  for (int i = 0; i < NB; ++i) printf(" %d", plan[i].region);
   printf("\n");
 
   hipFree(d_arena);
@@ -187,5 +238,6 @@ int main(int argc, char** argv) {
   free(m);
   free(v);
   free(flat);
+  free(cast);
   return 0;
 }

@@ -6,12 +6,9 @@
   master, m, v and the parameter slice on every call, against the oracle
   stepped chunk by chunk on the host (tests/_fullsize.py). The two 13B
   pipelines are also compared with each other on the device.
-* LLaMA-3 8B (AdamW, two groups): every element of the norm group and of a
-  chunk sample of the matrix group on every call -- every 64th 16M-element
-  chunk, the first and the last, every chunk holding a tensor boundary, and
-  every chunk past element 2^32, where the update kernel's grid (2^20 tiles of
-  4096 elements) starts its second round; the norm and the flag over all
-  elements.
+* LLaMA-3 8B (AdamW, two groups): every element of both groups on every
+  call, including the matrix group's elements past 2^32, where the update
+  kernel's grid (2^20 tiles of 4096 elements) starts its second round.
 * tiny (and its literal shape list): every element.
 * Rank 0 of the 7.5B and 13B shards (offset 0): a fixed sample of coordinates
   (first and last 64, tensor boundaries, 4096 random ones) stepped by the
@@ -251,22 +248,6 @@ def _free():
     torch.cuda.empty_cache()
 
 
-SAMPLE_CHUNK = 1 << 24        # the chunk of the large-shard sample (16M elements)
-SECOND_ROUND = 4096 << 20     # elements one update launch covers before its grid loops
-
-
-def llama_sample(n, boundaries):
-    """The LLaMA-3 matrix group's checked ranges: 16M-element chunks -- every
-    64th, the first, the last, every one holding a tensor boundary, and every
-    one that reaches past element 2^32 (the second grid-stride round of the
-    update kernel) -- as sorted disjoint [(start, end)]."""
-    last = (n - 1) // SAMPLE_CHUNK
-    pick = set(range(0, last + 1, 64)) | {0, last}
-    pick |= {b // SAMPLE_CHUNK for b in boundaries if 0 <= b < n}
-    pick |= set(range(max(0, (SECOND_ROUND - 1) // SAMPLE_CHUNK), last + 1))
-    return [(c * SAMPLE_CHUNK, min(n, (c + 1) * SAMPLE_CHUNK)) for c in sorted(pick)]
-
-
 class FullRun:
     """A workload at full size for one or two pipelines on the same gradient
     copies (laid out as bench.py lays them out: one arena over HBM's regions,
@@ -275,7 +256,7 @@ class FullRun:
     one compared with the oracle; the others are compared with it on the
     device, bit for bit."""
 
-    def __init__(self, key, pipelines=("fused",), max_grad_norm=0.0, sampled=False):
+    def __init__(self, key, pipelines=("fused",), max_grad_norm=0.0):
         gc.collect()          # a previous run's arena must be gone before this one takes all free memory
         torch.cuda.empty_cache()
         self.wl = wl = WORKLOADS[key]
@@ -340,9 +321,6 @@ class FullRun:
         for gi, (spec, (psi, off, n)) in enumerate(zip(wl.groups, shards)):
             g = main["groups"][gi]
             ranges = [(0, n)]
-            if sampled and n > SAMPLE_CHUNK:
-                bounds = [sl[1] for sl in zdp.partition_tensors(list(spec.numels), wl.n_d, wl.rank)]
-                ranges = llama_sample(n, bounds)
 
             def state(g=g):
                 return zdp.current_state(g, self.last_state)
@@ -544,9 +522,11 @@ def test_13b_nd8_clipping_every_element():
 
 
 @pytest.mark.timeout(1200)
-def test_llama3_8b_adamw_two_groups_chunk_sample():
+def test_llama3_8b_adamw_two_groups_every_element():
+    # 8,030,261,248 elements: the update kernel's grid (2^20 tiles of 4096) covers the matrix group's
+    # first 2^32 elements and loops over the rest; the oracle's copy of the state takes 112 GB of host memory
     print("[workload] llama3_8b", flush=True)
-    run = FullRun("llama3_8b", sampled=True)
+    run = FullRun("llama3_8b")
     st = run.run()
     assert st.step == 5
     _done(run)
