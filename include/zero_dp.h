@@ -318,6 +318,24 @@ int zero_grad_norm_overflow(const void* const* grads, const int64_t* counts, int
 int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_policy* policy,
                    void* workspace, size_t workspace_bytes, zero_step_state* state, void* stream);
 
+/* zero_adam_step without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same kernels and results, with the norm
+ * partials in a static device array of the library (8 MiB + 16 KiB,
+ * ZERO_MAX_GROUPS groups, any shard size) instead of a caller's workspace.
+ * Each GPU the library runs on holds one copy of that array until the process
+ * ends; its address is looked up on the first call on a device. The call
+ * allocates and frees nothing. Every call on a GPU shares that GPU's array,
+ * so calls that overlap on one GPU (concurrent streams, threads) race; order
+ * them. The contents need no initialisation (each call writes the partials it
+ * reads). Works for every pipeline; in the checked one the preceding
+ * zero_reduce_grad_segment / zero_grad_norm_overflow calls still take a
+ * workspace, since zero_adam_step reads only the state in that pipeline.
+ * Errors: as zero_adam_step; INVALID_ARG for n_groups beyond ZERO_MAX_GROUPS;
+ * HIP if the array's address cannot be found. */
+int zero_adam_step_static(const zero_group* groups, int32_t n_groups, const zero_policy* policy,
+                          zero_step_state* state, void* stream);
+
 /* Copy an fp32 master shard into the 16-bit flat vector [DeepSpeed
  * walkthrough §6 step 5]: flat_param[offset + j] = RNE16(master[j]) for j < n
  * (NaN becomes the canonical quiet NaN). Used at initialisation and to restore

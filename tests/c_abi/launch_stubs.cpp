@@ -24,5 +24,6 @@ hipError_t launch_redo_commit(const CommitArgs&, hipStream_t) { return never("re
 hipError_t launch_state_init(zero_step_state*, float, hipStream_t) { return never("state init"); }
 hipError_t launch_cast(const CastArgs&, bool, hipStream_t) { return never("cast"); }
 hipError_t launch_restore(const RestoreArgs&, bool, hipStream_t) { return never("restore"); }
+hipError_t static_scratch(void**) { return never("static scratch"); }
 
 }  // namespace zdp

@@ -29,7 +29,7 @@ ARENA_ALIGN = 2 << 20
 EXPORTS = ("zero_partition", "zero_partition_tensors", "zero_workspace_bytes",
            "zero_last_error", "zero_state_init", "zero_reduce_grad_segment",
            "zero_grad_norm_overflow", "zero_adam_step", "zero_cast_writeback", "zero_plan_arena",
-           "zero_set_grid_limit")
+           "zero_set_grid_limit", "zero_adam_step_static")
 
 
 class ZeroError(RuntimeError):
@@ -123,6 +123,7 @@ def load():
         L.zero_cast_writeback.argtypes = [vp, i64, vp, i64, i32, vp]
         L.zero_plan_arena.argtypes = [ctypes.POINTER(ArenaBuffer), i32, i64, i32, i64, ctypes.POINTER(i64)]
         L.zero_set_grid_limit.argtypes = [i32]
+        L.zero_adam_step_static.argtypes = [ctypes.POINTER(_Group), i32, ctypes.POINTER(Policy), vp, vp]
         for name in EXPORTS:
             fn = getattr(L, name)
             if name not in ("zero_workspace_bytes", "zero_last_error"):
@@ -463,6 +464,19 @@ def adam_step(groups, workspace, state, policy_=None, stream=None):
     sc = ctypes.byref(policy_) if policy_ is not None else None
     _check(load().zero_adam_step(arr, len(groups), sc, _ptr(workspace), _nbytes(workspace), _ptr(state),
                                  _stream(stream)))
+
+
+def adam_step_static(groups, state, policy_=None, stream=None):
+    """adam_step without a workspace: the library's static scratch holds the
+    norm partials (for callers that cannot allocate; calls that overlap on
+    one GPU race)."""
+    dev = _state_device(state)
+    keep = []
+    arr = _array_type(_Group, len(groups))()
+    for g, s in zip(groups, arr):
+        _group_struct(g, keep, s, dev)
+    sc = ctypes.byref(policy_) if policy_ is not None else None
+    _check(load().zero_adam_step_static(arr, len(groups), sc, _ptr(state), _stream(stream)))
 
 
 def current_state(group, state_dict):

@@ -601,6 +601,18 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_policy
   return e == hipSuccess ? ZERO_OK : hip_fail(e, "commit launch");
 }
 
+int zero_adam_step_static(const zero_group* groups, int32_t n_groups, const zero_policy* policy,
+                          zero_step_state* state, void* stream) {
+  if (n_groups < 1 || n_groups > ZERO_MAX_GROUPS)
+    return fail(ZERO_ERR_INVALID_ARG, "n_groups = %d out of [1, %d]: the static scratch holds the partials of at most %d "
+                "groups", n_groups, ZERO_MAX_GROUPS, ZERO_MAX_GROUPS);
+  if (int rc = check_device()) return rc;
+  void* ws = nullptr;
+  hipError_t e = static_scratch(&ws);
+  if (e != hipSuccess) return hip_fail(e, "address of the static scratch (hipGetSymbolAddress)");
+  return zero_adam_step(groups, n_groups, policy, ws, kWorkspaceBytes, state, stream);
+}
+
 int zero_set_grid_limit(int32_t max_blocks) {
   if (max_blocks < 0) return fail(ZERO_ERR_INVALID_ARG, "max_blocks = %d < 0", max_blocks);
   g_grid_limit.store(max_blocks, std::memory_order_relaxed);

@@ -206,6 +206,9 @@ hipError_t launch_commit(const CommitArgs& a, hipStream_t s);
 hipError_t launch_redo_commit(const CommitArgs& a, hipStream_t s);
 hipError_t launch_state_init(zero_step_state* st, float loss_scale, hipStream_t s);
 hipError_t launch_cast(const CastArgs& a, bool vec, hipStream_t s);
+// Device address (on the current device) of the kWorkspaceBytes static
+// scratch array that zero_adam_step_static uses instead of a workspace.
+hipError_t static_scratch(void** ptr);
 hipError_t launch_restore(const RestoreArgs& a, bool vec, hipStream_t s);
 
 }  // namespace zdp
