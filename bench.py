@@ -30,7 +30,8 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0
 DEFAULT_WORKLOAD = "llama3_8b"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "zero_dp_partitioned_amd", "csrc", "kernels.hip")
+CSRC = os.path.join(ROOT, "zero_dp_partitioned_amd", "csrc")
+KERNEL_SRCS = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "zero_dp_internal.h")]
 
 
 def bytes_per_param(n_d):
@@ -39,10 +40,11 @@ def bytes_per_param(n_d):
 
 
 def kernel_source_hash():
-    """Hash of the kernel source's code: comments and whitespace are removed
-    first, so that only a change to the code invalidates recorded counters."""
+    """Hash of the kernels' code and of the header that fixes their launch
+    shapes (tile sizes, grid caps): comments and whitespace are removed first,
+    so that only a change to the code invalidates recorded counters."""
     import re
-    src = open(KERNEL_SRC).read()
+    src = "\n".join(open(f).read() for f in KERNEL_SRCS)
     src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
     src = re.sub(r"//[^\n]*", " ", src)
     src = " ".join(src.split())

@@ -190,7 +190,7 @@ int zero_partition_tensors(const int64_t* numels, int32_t n_tensors, int32_t n_d
                            int32_t cap, int32_t* n_out);
 
 /* Bytes of device workspace the step calls need for up to n_groups groups:
- * the gradient-norm partials (about 8 MiB, the same for any shard size and
+ * the gradient-norm partials (about 16 MiB, the same for any shard size and
  * any n_groups in range). 0 if n_groups is out of range. The workspace must
  * be 256-byte aligned; its contents need no initialisation. Every call that
  * takes a workspace also takes its size and returns ZERO_ERR_WORKSPACE if it
@@ -321,7 +321,7 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_policy
 /* zero_adam_step without a workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc): the same kernels and results, with the norm
- * partials in a static device array of the library (8 MiB + 16 KiB,
+ * partials in a static device array of the library (16 MiB + 16 KiB,
  * ZERO_MAX_GROUPS groups, any shard size) instead of a caller's workspace.
  * Each GPU the library runs on holds one copy of that array until the process
  * ends; its address is looked up on the first call on a device. The call
@@ -346,7 +346,7 @@ int zero_cast_writeback(const float* master, int64_t n, void* flat_param, int64_
 /* ---- testing --------------------------------------------------------------
  * Not an operation of the pages. Caps the blocks of every streaming launch
  * (update, second pass, averaging, scan, restore, cast) at max_blocks > 0, on
- * top of each launch's own cap (2^20 tiles per launch; 65,536 blocks for the
+ * top of each launch's own cap (2^21 tiles per launch; 65,536 blocks for the
  * second pass and the scan; 1,024 for the restore). Every streaming kernel
  * loops over the tiles its grid does not cover, so a small shard under a low
  * cap runs the same grid-stride loops that otherwise only shards of billions

@@ -17,7 +17,7 @@
  *           Models" reading notes, second part §3 (per-coordinate Adam update)
  *           and §4 (all-reduce = reduce-scatter then all-gather; the averaged
  *           shard formula).
- *   [PAPER] Chinese translation of the ZeRO paper, §3.1 (mixed-precision
+ *   [ZERO-ZH] Chinese translation of the ZeRO paper, §3.1 (mixed-precision
  *           Adam: fp16 params/grads, fp32 master, momentum, variance).
  *
  * Readings where the pages are silent (each listed in the design notes):
@@ -291,7 +291,7 @@ static double beta_pow(double beta, int64_t t)
 /* One Adam/AdamW update of n coordinates for applied step t (t >= 1), on the
  * rank's fp32 master/m/v shard, followed by the fp32 -> 16-bit copy into the
  * rank's slice of the flat parameter vector [NOTES §3 update equations;
- * DS12 §6 steps 3-5; PAPER §3.1 for the fp32 state]. `param` points at the
+ * DS12 §6 steps 3-5; ZERO-ZH §3.1 for the fp32 state]. `param` points at the
  * first element of the rank's slice (NULL: no writeback). `clip` multiplies
  * the unscaled gradient (DS12 §6 step 3 unscales and clips; 1 = no clip). */
 void oracle_adam_update(int64_t n, const float *a, float inv_scale, float clip,

@@ -7,8 +7,9 @@
   stepped chunk by chunk on the host (tests/_fullsize.py). The two 13B
   pipelines are also compared with each other on the device.
 * LLaMA-3 8B (AdamW, two groups): every element of both groups on every
-  call, including the matrix group's elements past 2^32, where the update
-  kernel's grid (2^20 tiles of 4096 elements) starts its second round.
+  call, with one block per 4096-element tile, and on the last two calls with
+  the grid capped at 2^20 blocks, so that blocks loop over a second tile past
+  element 2^32.
 * tiny (and its literal shape list): every element.
 * Rank 0 of the 7.5B and 13B shards (offset 0): a fixed sample of coordinates
   (first and last 64, tensor boundaries, 4096 random ones) stepped by the
@@ -378,16 +379,25 @@ class FullRun:
                 i = int(torch.nonzero(x != y)[0])
                 raise AssertionError(f"{tag}: pipelines differ at element {s + i}: {int(x[i])} vs {int(y[i])}")
 
-    def run(self, steps=None):
+    def run(self, steps=None, grid_limits=None):
+        """Step ``steps`` times; ``grid_limits`` maps a call to a block cap
+        (zdp.set_grid_limit) that holds for that call's launches only."""
         wl = self.wl
         steps = wl.steps if steps is None else steps
         main = self.pipelines[-1]
         for call in range(1, steps + 1):
             t0 = time.perf_counter()
             self.draw_grads(call)
-            for p in self.pipelines:
-                self.gpu_step(p)
-            torch.cuda.synchronize()
+            limit = (grid_limits or {}).get(call, 0)
+            if limit:
+                print(f"  call {call}: at most {limit} blocks per launch", flush=True)
+            zdp.set_grid_limit(limit)
+            try:
+                for p in self.pipelines:
+                    self.gpu_step(p)
+                torch.cuda.synchronize()
+            finally:
+                zdp.set_grid_limit(0)
             states = {p: zdp.read_state(self.side[p]["state"]) for p in self.pipelines}
             s = states[main]
             tag = f"{wl.key} call {call}"
@@ -523,10 +533,11 @@ def test_13b_nd8_clipping_every_element():
 
 @pytest.mark.timeout(1200)
 def test_llama3_8b_adamw_two_groups_every_element():
-    # 8,030,261,248 elements: the update kernel's grid (2^20 tiles of 4096) covers the matrix group's
-    # first 2^32 elements and loops over the rest; the oracle's copy of the state takes 112 GB of host memory
+    # 8,030,261,248 elements, one block per 4096-element tile (1,960,448 blocks for the matrix group);
+    # on the last two calls a cap of 2^20 blocks makes 911,872 blocks loop over a second tile, past
+    # element 2^32. The oracle's copy of the state takes 112 GB of host memory.
     print("[workload] llama3_8b", flush=True)
     run = FullRun("llama3_8b")
-    st = run.run()
+    st = run.run(grid_limits={4: 1 << 20, 5: 1 << 20})
     assert st.step == 5
     _done(run)

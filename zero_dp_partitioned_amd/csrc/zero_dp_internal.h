@@ -37,7 +37,7 @@ constexpr int kCappedReduceCopies = 8;
 // blocks resident per compute unit. Residency is capped by giving each block
 // an otherwise unused share of the CU's LDS (batch_lds_bytes).
 constexpr int kBatchBlocksPerCU = 2;
-constexpr int kMaxGrid = 1 << 20;                    // blocks per launch (tiles beyond: grid-stride)
+constexpr int kMaxGrid = 1 << 21;                    // blocks per launch (tiles beyond: grid-stride)
 constexpr int kInlineReplicas = 64;                  // replica pointers carried in the kernel arguments
 
 // Workspace: [0, kHeaderBytes) per-group level-2 norm partials, then one fp64
