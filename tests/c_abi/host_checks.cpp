@@ -151,11 +151,25 @@ static void device_call_checks() {
   EXPECT(zdp::stream_grid(int64_t(1) << 40) == zdp::kMaxGrid && zdp::stream_grid(4097) == 2);
 }
 
+// Which launches take the batched schedule (update) and the batched read
+// (averaging pass), and the LDS share that caps their residency.
+static void launch_shapes() {
+  using namespace zdp;
+  EXPECT(!batched(kSrcF16, true, 1) && batched(kSrcF16, true, 2) && batched(kSrcBF16, true, 31));
+  EXPECT(!batched(kSrcF16, true, 32) && !batched(kSrcAvg, true, 8) && !batched(kSrcF16, false, 8));
+  EXPECT(!reduce_batched(true, 7) && reduce_batched(true, 8) && reduce_batched(true, 32));
+  EXPECT(!reduce_batched(true, 33) && !reduce_batched(false, 16));
+  const size_t b160 = batch_lds_bytes(160u << 10), b64 = batch_lds_bytes(64u << 10);
+  EXPECT(b160 == (64u << 10) && 2 * (b160 + 1024) <= (160u << 10) && 3 * b160 > (160u << 10));
+  EXPECT(b64 % 256 == 0 && 2 * (b64 + 1024) <= (64u << 10) && 3 * b64 > (64u << 10));
+}
+
 int main() {
   partitions();
   slices();
   arenas();
   device_call_checks();
+  launch_shapes();
   if (failures) {
     fprintf(stderr, "host checks: %d failure(s)\n", failures);
     return 1;

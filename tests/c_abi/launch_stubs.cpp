@@ -14,7 +14,7 @@ static hipError_t never(const char* what) {
 }
 
 hipError_t launch_adam(const AdamArgs&, int, bool, int, size_t, hipStream_t, int*) { return never("adam"); }
-hipError_t launch_reduce(const ReduceArgs&, int, bool, hipStream_t, int*) { return never("reduce"); }
+hipError_t launch_reduce(const ReduceArgs&, int, bool, size_t, hipStream_t, int*) { return never("reduce"); }
 hipError_t launch_scan(const ReduceArgs&, int, hipStream_t, int*) { return never("scan"); }
 int scan_grid(int64_t) { return 1; }
 hipError_t launch_fold(const FoldArgs&, hipStream_t) { return never("fold"); }

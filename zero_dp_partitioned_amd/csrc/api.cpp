@@ -343,7 +343,8 @@ int zero_reduce_grad_segment(const void* const* replicas, int32_t n_d, int32_t g
   if (group < 0 || group >= ZERO_MAX_GROUPS) return fail(ZERO_ERR_WORKSPACE, "group %d out of range", group);
   ReduceArgs R;
   if (int rc = make_source(replicas, n_d, grad_dt, n, &R.src)) return rc;
-  if (int rc = check_device()) return rc;
+  DeviceInfo dev;
+  if (int rc = check_device(&dev)) return rc;
   HeadCheck hc;
   hc.add(avg_out, 4);
   for (int32_t r = 0; r < n_d && n > 0; ++r) hc.add(replicas[r], 2);
@@ -355,7 +356,7 @@ int zero_reduce_grad_segment(const void* const* replicas, int32_t n_d, int32_t g
   R.partials = scratch_of(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   int blocks = 0;
-  hipError_t e = launch_reduce(R, grad_dt == ZERO_DT_BF16 ? kSrcBF16 : kSrcF16, vec, s, &blocks);
+  hipError_t e = launch_reduce(R, grad_dt == ZERO_DT_BF16 ? kSrcBF16 : kSrcF16, vec, dev.batch_lds, s, &blocks);
   if (e != hipSuccess) return hip_fail(e, "reduce launch");
   e = fold_into(workspace, group, blocks, s);
   return e == hipSuccess ? ZERO_OK : hip_fail(e, "fold launch");
@@ -400,7 +401,8 @@ int zero_grad_norm_overflow(const void* const* grads, const int64_t* counts, int
     const bool wide = aligned(grads[g], 16);
     if (wide) R[g].head = 0;
     int blocks = 0;
-    hipError_t e = wide ? launch_scan(R[g], src, s, &blocks) : launch_reduce(R[g], src, vec[g], s, &blocks);
+    // (one copy: the averaging launch never takes the batched read, so it needs no LDS share)
+    hipError_t e = wide ? launch_scan(R[g], src, s, &blocks) : launch_reduce(R[g], src, vec[g], 0, s, &blocks);
     if (e != hipSuccess) return hip_fail(e, "scan launch");
     e = fold_into(workspace, g, blocks, s);
     if (e != hipSuccess) return hip_fail(e, "fold launch");

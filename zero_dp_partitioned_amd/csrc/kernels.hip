@@ -786,9 +786,9 @@ hipError_t adam_launch(const AdamArgs& a, size_t batch_lds, hipStream_t s, int* 
 }
 
 template <int SRC, bool VEC, int INFL>
-hipError_t reduce_launch(const ReduceArgs& a, hipStream_t s, int* blocks) {
+hipError_t reduce_launch(const ReduceArgs& a, size_t lds, hipStream_t s, int* blocks) {
   *blocks = stream_grid(a.n - a.head, kQuadsPerThread);
-  hipLaunchKernelGGL((reduce_kernel<SRC, VEC, kQuadsPerThread, INFL>), dim3(*blocks), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL((reduce_kernel<SRC, VEC, kQuadsPerThread, INFL>), dim3(*blocks), dim3(kBlock), lds, s, a);
   return hipGetLastError();
 }
 
@@ -837,17 +837,22 @@ hipError_t launch_restore(const RestoreArgs& a, bool vec, hipStream_t s) {
 }
 
 // The averaging pass keeps 4 quads per lane at every N_d (it has no state
-// streams, and the wide read measured slower there); from kCappedReduceCopies
-// copies up it caps the gradient loads in flight.
-hipError_t launch_reduce(const ReduceArgs& a, int src, bool vec, hipStream_t s, int* blocks) {
-  const bool capped = vec && a.src.n_d >= kCappedReduceCopies;
+// streams, and the wide read measured slower there). From kCappedReduceCopies
+// to kWideCopies copies it issues every load of a tile at once with residency
+// capped at kBatchBlocksPerCU blocks per CU by batch_lds bytes of otherwise
+// unused LDS; above that it caps the gradient loads in flight instead; below
+// it, eight copies' loads at once at full residency.
+hipError_t launch_reduce(const ReduceArgs& a, int src, bool vec, size_t batch_lds, hipStream_t s, int* blocks) {
+  const bool batch = reduce_batched(vec, a.src.n_d);
+  const bool capped = vec && !batch && a.src.n_d >= kCappedReduceCopies;
+  const size_t lds = batch ? batch_lds : 0;
   if (src == kSrcF16) {
-    if (capped) return reduce_launch<kSrcF16, true, kWideInflight>(a, s, blocks);
-    return vec ? reduce_launch<kSrcF16, true, 0>(a, s, blocks) : reduce_launch<kSrcF16, false, 0>(a, s, blocks);
+    if (capped) return reduce_launch<kSrcF16, true, kWideInflight>(a, 0, s, blocks);
+    return vec ? reduce_launch<kSrcF16, true, 0>(a, lds, s, blocks) : reduce_launch<kSrcF16, false, 0>(a, 0, s, blocks);
   }
   if (src == kSrcBF16) {
-    if (capped) return reduce_launch<kSrcBF16, true, kWideInflight>(a, s, blocks);
-    return vec ? reduce_launch<kSrcBF16, true, 0>(a, s, blocks) : reduce_launch<kSrcBF16, false, 0>(a, s, blocks);
+    if (capped) return reduce_launch<kSrcBF16, true, kWideInflight>(a, 0, s, blocks);
+    return vec ? reduce_launch<kSrcBF16, true, 0>(a, lds, s, blocks) : reduce_launch<kSrcBF16, false, 0>(a, 0, s, blocks);
   }
   return hipErrorInvalidValue;
 }

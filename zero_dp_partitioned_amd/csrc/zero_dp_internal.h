@@ -27,9 +27,12 @@ constexpr int kQuadsWide = 8;
 constexpr int kWideCopies = 32;
 constexpr int kWideInflight = 3;
 constexpr int tile_inflight(int quads) { return quads == kQuadsWide ? kWideInflight : 0; }
-// The averaging pass (checked pipeline) keeps 4 quads per lane; from
-// kCappedReduceCopies copies up its waves also keep at most kWideInflight
-// gradient loads in flight (1-4 % faster there, no gain with fewer copies).
+// The averaging pass (checked pipeline) keeps 4 quads per lane. With
+// kCappedReduceCopies to kWideCopies copies it takes the batched read: every
+// load of a tile in flight at once, at most kBatchBlocksPerCU blocks per CU
+// (reduce_batched); with more copies its waves keep at most kWideInflight
+// gradient loads in flight at full residency; with fewer, eight copies' loads
+// at once at full residency.
 constexpr int kCappedReduceCopies = 8;
 // With 2 to kWideCopies - 1 copies the update kernel takes the batched
 // schedule (see adam_kernel): every load of a tile in flight at once, then the
@@ -196,7 +199,12 @@ inline size_t batch_lds_bytes(size_t lds_per_cu) {
   b = b > 1024 ? (b - 1024) / 256 * 256 : 0;
   return b < (64u << 10) ? b : (64u << 10);
 }
-hipError_t launch_reduce(const ReduceArgs& a, int src_kind, bool vec, hipStream_t s, int* blocks);
+// Whether an averaging launch takes the batched read (batch_lds as above).
+inline bool reduce_batched(bool vec, int n_d) {
+  return vec && n_d >= kCappedReduceCopies && n_d <= kWideCopies;
+}
+hipError_t launch_reduce(const ReduceArgs& a, int src_kind, bool vec, size_t batch_lds, hipStream_t s,
+                         int* blocks);
 // Single-copy scan (partials only) of a 16-byte-aligned copy; scan_grid(n) blocks, one partial each.
 hipError_t launch_scan(const ReduceArgs& a, int src_kind, hipStream_t s, int* blocks);
 int scan_grid(int64_t n);
