@@ -143,6 +143,8 @@ FUSED_CASES = [
     (65_541, 64, "bf16", 12, 0, "strided"),
     (30_001, 65, "f16", 0, 0, "strided"),
     (30_001, 100, "bf16", 2, 0, "strided"),
+    (40_961, 31, "bf16", 3, 0, "table"),        # 31 copies: the batched schedule's last count, division by N_d
+    (50_001, 16, "f16", 0, 0, "strided"),       # 16 copies, batched, 12 full tiles + a ragged tail
     (40_961, 32, "f16", 2, 0, "table"),         # 32+ copies: tiles of 8192, five full + a ragged tail
     (24_577, 48, "bf16", 0, 0, "table"),        # 48 copies: division by N_d, three wide tiles + tail
     (8_191, 32, "f16", 1, 0, "strided"),        # under one wide tile: the tail path only
@@ -335,7 +337,10 @@ def test_cast_writeback(dt, off):
 
 @pytest.mark.parametrize("n_d,dt,layout", [(1, "bf16", "table"), (4, "f16", "table"), (64, "f16", "strided"),
                                            (3, "bf16", "packed"), (100, "f16", "strided"), (8, "f16", "shift2"),
-                                           (1, "bf16", "shift1")])
+                                           (1, "bf16", "shift1"),
+                                           # either side of the batched read's range (8 to 32 copies)
+                                           (7, "bf16", "table"), (8, "bf16", "packed"), (32, "f16", "table"),
+                                           (33, "bf16", "strided"), (16, "f16", "shift1")])
 def test_reduce_grad_segment(n_d, dt, layout):
     n = 70_001
     reps = [grads16_np(n, dt, 1.0, (11, r)) for r in range(n_d)]
