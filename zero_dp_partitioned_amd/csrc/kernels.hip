@@ -8,11 +8,16 @@
 // run. One block per tile: the hardware dispatcher hands out tiles in order,
 // which keeps the resident blocks on one advancing window of HBM; on gfx950
 // this sustains clearly more bandwidth for a read-modify-write stream than a
-// resident grid looping over the vector. With 32 or more gradient copies the
-// update kernel's lanes take 8 quads (8192-element tiles) and read the copies
-// one after another with a cap on the loads in flight (source_tile). Arrays
-// that all start at the same offset modulo 4 elements run the quad path after
-// a head of up to 3 elements that block 0 updates one by one.
+// resident grid looping over the vector (launches beyond 2^21 tiles do loop).
+// With 32 or more gradient copies the update kernel's lanes take 8 quads
+// (8192-element tiles) and read the copies one after another with a cap on
+// the loads in flight (source_tile). With 2 to 31 copies it takes the batched
+// schedule instead: a whole tile's loads in flight at once, then the
+// arithmetic, then the stores array by array, at two blocks per CU (a dynamic
+// LDS share the kernel never touches caps the residency); the averaging pass
+// reads that way from 8 to 32 copies. Arrays that all start at the same offset
+// modulo 4 elements run the quad path after a head of up to 3 elements that
+// block 0 updates one by one.
 //
 // Numerics follow the per-coordinate Adam update of the ZeRO reading notes
 // (second part, §3) in fp32 with one rounding per operation: fp-contract is off
