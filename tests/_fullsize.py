@@ -43,6 +43,85 @@ def chunk_for(n_d):
     return max(4096, c)
 
 
+SAMPLE_CHUNK = 1 << 24         # elements per chunk of the fallback sample (host memory short)
+SAMPLE_EVERY = 64              # the sample keeps every 64th such chunk
+
+
+def host_bytes_available():
+    """Host memory this process can still take: MemAvailable, capped by the
+    room under the cgroup's memory limit when one is set (None if neither
+    can be read)."""
+    avail = None
+    try:
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemAvailable:"):
+                    avail = int(line.split()[1]) * 1024
+    except OSError:
+        pass
+    for lim, cur in (("/sys/fs/cgroup/memory.max", "/sys/fs/cgroup/memory.current"),
+                     ("/sys/fs/cgroup/memory/memory.limit_in_bytes", "/sys/fs/cgroup/memory/memory.usage_in_bytes")):
+        try:
+            with open(lim) as f:
+                limit = f.read().strip()
+            with open(cur) as f:
+                used = int(f.read().strip())
+        except (OSError, ValueError):
+            continue
+        if limit.isdigit():
+            room = int(limit) - used
+            avail = room if avail is None else min(avail, room)
+        break
+    return avail
+
+
+def oracle_bytes(n, verdict_first):
+    """Host bytes of the oracle's copy of n checked elements: fp32 master, m
+    and v and the 16-bit parameters, plus the fp32 averages pass A keeps when
+    the verdict comes first."""
+    return n * (12 + 2 + (4 if verdict_first else 0))
+
+
+def sample_ranges(n, boundaries, chunk=SAMPLE_CHUNK, every=SAMPLE_EVERY):
+    """The fallback sample of a shard of n elements, as sorted disjoint
+    [(start, end)]: every `every`-th chunk of `chunk` elements, the first and
+    the last chunk, and every chunk holding one of `boundaries` (tensor or
+    group boundaries, element offsets into the shard)."""
+    if n <= 0:
+        return []
+    last = (n - 1) // chunk
+    ids = set(range(0, last + 1, every)) | {0, last}
+    ids |= {b // chunk for b in boundaries if 0 <= b < n}
+    out = []
+    for i in sorted(ids):
+        s, e = i * chunk, min(n, (i + 1) * chunk)
+        if out and out[-1][1] == s:
+            out[-1] = (out[-1][0], e)
+        else:
+            out.append((s, e))
+    return out
+
+
+def plan_ranges(shards, verdict_first, workers, available):
+    """What the oracle checks element by element in each shard: all of it,
+    or, when its copy of the state would not fit in 80 % of the host memory
+    still available (staging buffers included), the fallback sample.
+    `shards` is [(n, boundaries)]; returns ([ranges per shard], message)."""
+    need = sum(oracle_bytes(n, verdict_first) for n, _ in shards) + (workers + 4) * STAGE_BYTES
+    full = [[(0, n)] if n else [] for n, _ in shards]
+    if available is None or need <= 0.8 * available:
+        return full, None
+    ranges = [sample_ranges(n, b) for n, b in shards]
+    kept = sum(e - s for r in ranges for s, e in r)
+    total = sum(n for n, _ in shards)
+    msg = (f"host memory short: every element needs {need / 2**30:.1f} GiB of host memory and "
+           f"{available / 2**30:.1f} GiB is available, so only a chunk sample is compared element by "
+           f"element ({kept} of {total} elements: every {SAMPLE_EVERY}th chunk of {SAMPLE_CHUNK}, the first "
+           f"and last chunks and those holding tensor or group boundaries); norm and flag still cover "
+           f"every element")
+    return ranges, msg
+
+
 def cpu_workers():
     """Threads for the oracle: the CPU share of this process (affinity mask,
     capped by OMP_NUM_THREADS when set)."""

@@ -4,12 +4,14 @@ unchunked oracle run over the whole shard. The chunked harness must agree
 with it exactly over several calls (static scale in one pass; dynamic scale
 with an overflowing call, and clipping, in two passes; two groups; a chunk
 sample), and must catch a single planted one-ulp difference anywhere,
-naming the chunk."""
+naming the chunk. Also the fallback plan for a host short of memory: which
+chunks it samples and when it is taken."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
+import _fullsize as _fs
 from _fullsize import FullCheck, GroupCheck, HostStager
 from _parity import Bar
 from workloads import grads16_np, normal_f32_np, to16_bits_np
@@ -111,3 +113,41 @@ def test_a_chunk_sample_still_takes_the_norm_over_every_element():
 def test_a_single_planted_ulp_is_caught(policy, where):
     with pytest.raises(AssertionError, match=r"elements \[\d+, \d+\) master"):
         _run(policy, calls=2, plant=(2, *where))
+
+
+# --------------------------------------------------------------------------
+# the fallback when the host cannot hold the oracle's copy of every element
+# --------------------------------------------------------------------------
+
+def test_sample_ranges_cover_the_sampled_chunks_in_order():
+    c = _fs.SAMPLE_CHUNK
+    n = 300 * c + 5
+    r = _fs.sample_ranges(n, [3 * c + 7, 130 * c, n - 1, n, -1])
+    assert r == [(0, c), (3 * c, 4 * c), (64 * c, 65 * c), (128 * c, 129 * c), (130 * c, 131 * c),
+                 (192 * c, 193 * c), (256 * c, 257 * c), (300 * c, n)]
+    assert _fs.sample_ranges(0, [0]) == []
+    assert _fs.sample_ranges(10, []) == [(0, 10)]
+    assert _fs.sample_ranges(3 * c, [c]) == [(0, 3 * c)]     # adjacent sampled chunks merge
+
+
+def test_plan_ranges_falls_back_only_when_the_state_does_not_fit():
+    shards = [(1_000_000, [10]), (300, [])]
+    need = _fs.oracle_bytes(1_000_300, False) + 20 * _fs.STAGE_BYTES
+    full, msg = _fs.plan_ranges(shards, False, 16, int(need / 0.8) + 1)
+    assert msg is None and full == [[(0, 1_000_000)], [(0, 300)]]
+    full, msg = _fs.plan_ranges(shards, False, 16, None)
+    assert msg is None and full == [[(0, 1_000_000)], [(0, 300)]]
+    part, msg = _fs.plan_ranges(shards, True, 16, int(need / 0.8) + 1)   # the kept averages tip it over
+    assert msg and "chunk sample" in msg and part == [_fs.sample_ranges(1_000_000, [10]), [(0, 300)]]
+
+
+@pytest.mark.parametrize("where,caught", [(500, True), (2000, False)])
+def test_a_sampled_run_compares_only_its_chunks(where, caught):
+    """A planted difference inside the sample is caught; one outside it is
+    not looked at (its element still enters the norm, unchanged)."""
+    ranges = {0: [(0, 1024), (3072, 4096)]}
+    if caught:
+        with pytest.raises(AssertionError, match=r"elements \[\d+, \d+\) master"):
+            _run(oracle.Policy(), calls=2, ranges=ranges, plant=(2, 0, where))
+    else:
+        assert _run(oracle.Policy(), calls=2, ranges=ranges, plant=(2, 0, where)).step == 2

@@ -33,7 +33,7 @@ import zero_dp_partitioned_amd as zdp
 from zero_dp_partitioned_amd import layout
 from workloads import WORKLOADS, derive_seed, fill_normal_, torch_dtype
 
-from _fullsize import FullCheck, GroupCheck, chunk_for
+from _fullsize import FullCheck, GroupCheck, chunk_for, cpu_workers, host_bytes_available, plan_ranges
 from _gpu_helpers import DEV, ORACLE_DT, assert_bits_equal, assert_u16_equal, down16, down32
 from _parity import Bar
 
@@ -315,13 +315,22 @@ class FullRun:
                            if needs_norm else None)
             if p == "checked" and wl.n_d > 1:
                 d["avg"] = [buf[(p, gi, "avg")][:g.master.numel()] for gi, g in enumerate(d["groups"])]
-        # the oracle's side: the last pipeline, element by element
+        # the oracle's side: the last pipeline, element by element (or a chunk sample if the host
+        # cannot hold the oracle's copy of every element's state)
         main = self.side[pipelines[-1]]
         self.last_state = {"cur": 0}
         checks = []
+        bounds = []
+        for spec, (psi, off, n) in zip(wl.groups, shards):
+            ends = np.cumsum(np.array(spec.numels, dtype=np.int64)) - off
+            bounds.append((n, [int(x) for x in ends if 0 < x < n] + [1 << 32]))
+        plan, msg = plan_ranges(bounds, wl.dynamic_loss_scale or max_grad_norm > 0, min(16, cpu_workers()),
+                                host_bytes_available())
+        if msg:
+            print(f"  {msg}", flush=True)
         for gi, (spec, (psi, off, n)) in enumerate(zip(wl.groups, shards)):
             g = main["groups"][gi]
-            ranges = [(0, n)]
+            ranges = plan[gi]
 
             def state(g=g):
                 return zdp.current_state(g, self.last_state)
