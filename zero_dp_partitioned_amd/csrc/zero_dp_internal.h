@@ -38,7 +38,9 @@ constexpr int kCappedReduceCopies = 8;
 // schedule (see adam_kernel): every load of a tile in flight at once, then the
 // arithmetic, then the stores array by array, with at most kBatchBlocksPerCU
 // blocks resident per compute unit. Residency is capped by giving each block
-// an otherwise unused share of the CU's LDS (batch_lds_bytes).
+// an otherwise unused share of the CU's LDS (batch_lds_bytes). The update from
+// an fp32 average (checked pipeline) keeps the per-quad schedule but runs at
+// the same residency.
 constexpr int kBatchBlocksPerCU = 2;
 constexpr int kMaxGrid = 1 << 21;                    // blocks per launch (tiles beyond: grid-stride)
 constexpr int kInlineReplicas = 64;                  // replica pointers carried in the kernel arguments
