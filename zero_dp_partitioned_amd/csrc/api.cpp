@@ -106,8 +106,10 @@ double* level2_of(void* ws, int32_t g) { return static_cast<double*>(ws) + stati
 double* scratch_of(void* ws) { return reinterpret_cast<double*>(static_cast<char*>(ws) + kHeaderBytes); }
 
 // Reduce the `blocks` partials a launch just wrote into the level-2 partials
-// of group g (the launchers report their grid size).
+// of group g (the launchers report their grid size, or 0 when a small launch
+// wrote the level-2 partials itself: then there is nothing to fold).
 hipError_t fold_into(void* ws, int32_t g, int64_t blocks, hipStream_t s) {
+  if (blocks == 0) return hipSuccess;
   FoldArgs F;
   F.partials = scratch_of(ws);
   F.count = blocks;
@@ -354,6 +356,7 @@ int zero_reduce_grad_segment(const void* const* replicas, int32_t n_d, int32_t g
   R.avg_out = avg_out;
   R.state = state;
   R.partials = scratch_of(workspace);
+  R.level2 = level2_of(workspace, group);
   hipStream_t s = static_cast<hipStream_t>(stream);
   int blocks = 0;
   hipError_t e = launch_reduce(R, grad_dt == ZERO_DT_BF16 ? kSrcBF16 : kSrcF16, vec, dev.batch_lds, s, &blocks);
@@ -385,6 +388,7 @@ int zero_grad_norm_overflow(const void* const* grads, const int64_t* counts, int
       R[g].avg_out = nullptr;
       R[g].state = state;
       R[g].partials = scratch_of(workspace);
+      R[g].level2 = level2_of(workspace, g);
       HeadCheck hc;
       hc.add(grads[g], 2);
       vec[g] = true;  // one array: a head of h < 4 elements always aligns it
@@ -505,6 +509,7 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_policy
     a.group = g;
     a.state = state;
     a.partials = checked ? nullptr : scratch_of(workspace);
+    a.level2 = checked ? nullptr : level2_of(workspace, g);
     vec[g] = v;
   }
   DeviceInfo dev;
@@ -564,6 +569,7 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_policy
       for (int32_t g = 0; g < n_groups; ++g) {
         AdamArgs a = A[g];
         a.partials = nullptr;
+        a.level2 = nullptr;
         int blocks = 0;
         e = launch_adam(a, src[g], vec[g], kRedo, dev.batch_lds, s, &blocks);
         if (e != hipSuccess) return hip_fail(e, "second-pass launch");

@@ -281,7 +281,9 @@ __device__ __forceinline__ void account(float a, float g, double& sumsq, int& ba
 
 // One fp64 partial per block: wavefront butterfly, then the block's four
 // wavefronts through LDS in a fixed order. NaN marks a non-finite gradient.
-__device__ __forceinline__ void write_block_partial(double s, int bad, double* out) {
+// With fill > gridDim.x (a small launch writing a group's level-2 partials
+// directly) the blocks also zero the slots [gridDim.x, fill), each once.
+__device__ __forceinline__ void write_block_partial(double s, int bad, double* out, int fill) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
   const int any_bad = __any(bad);
@@ -302,6 +304,7 @@ __device__ __forceinline__ void write_block_partial(double s, int bad, double* o
       f |= wf[k];
     }
     out[blockIdx.x] = f ? __builtin_nan("") : t;
+    for (int k = blockIdx.x + gridDim.x; k < fill; k += gridDim.x) out[k] = 0.0;
   }
 }
 
@@ -474,7 +477,7 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs A) {
       }
     }
   }
-  if constexpr (!CLIPPED) write_block_partial(sumsq, bad, A.partials);
+  if constexpr (!CLIPPED) write_block_partial(sumsq, bad, A.partials, A.fill);
 }
 
 // ------------------------------------------------------------------------
@@ -533,7 +536,7 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(const ReduceArgs R) {
       }
     }
   }
-  write_block_partial(sumsq, bad, R.partials);
+  write_block_partial(sumsq, bad, R.partials, R.fill);
 }
 
 // ------------------------------------------------------------------------
@@ -572,7 +575,7 @@ __global__ void __launch_bounds__(kBlock) scan_kernel(const ReduceArgs R) {
       }
     }
   }
-  write_block_partial(sumsq, bad, R.partials);
+  write_block_partial(sumsq, bad, R.partials, R.fill);
 }
 
 // ------------------------------------------------------------------------
@@ -773,14 +776,33 @@ __global__ void __launch_bounds__(kBlock) restore_kernel(const RestoreArgs R) {
   }
 }
 
+// A launch of at most kFoldBlocks blocks with the group's level-2 partials at
+// hand writes them itself: block b's partial into slot b, zeros into the
+// slots past its grid. That is what the fold would write: with one partial
+// per slot, its sums only add zeros, which changes no bit (a partial, a sum
+// of squares from +0, is never -0). *blocks = 0 then tells the caller that
+// nothing is left to fold; otherwise it is the grid.
+template <typename Args>
+Args route_partials(const Args& a, int grid, int* blocks) {
+  Args b = a;
+  b.fill = 0;
+  *blocks = grid;
+  if (a.level2 && a.partials && grid <= kFoldBlocks) {
+    b.partials = a.level2;
+    b.fill = kFoldBlocks;
+    *blocks = 0;
+  }
+  return b;
+}
+
 // The batched schedule (2 to 31 copies, 4-quad tiles) gets `batch_lds` bytes
 // of dynamic LDS per block, which it never touches: it caps the blocks
 // resident per CU at kBatchBlocksPerCU.
 template <int SRC, bool VEC, int MODE, int QL>
-hipError_t adam_launch(const AdamArgs& a, size_t batch_lds, hipStream_t s, int* blocks) {
-  int grid = stream_grid(a.n - a.head, QL);
+hipError_t adam_launch(const AdamArgs& args, size_t batch_lds, hipStream_t s, int* blocks) {
+  int grid = stream_grid(args.n - args.head, QL);
   if (MODE == kRedo && grid > kRedoGrid) grid = kRedoGrid;
-  *blocks = grid;
+  const AdamArgs a = route_partials(args, grid, blocks);
   if constexpr (QL == kQuadsPerThread && VEC && SRC != kSrcAvg) {
     if (batched(SRC, VEC, a.src.n_d)) {
       hipLaunchKernelGGL((adam_kernel<SRC, VEC, MODE, QL, true>), dim3(grid), dim3(kBlock), batch_lds, s, a);
@@ -795,9 +817,10 @@ hipError_t adam_launch(const AdamArgs& a, size_t batch_lds, hipStream_t s, int* 
 }
 
 template <int SRC, bool VEC, int INFL>
-hipError_t reduce_launch(const ReduceArgs& a, size_t lds, hipStream_t s, int* blocks) {
-  *blocks = stream_grid(a.n - a.head, kQuadsPerThread);
-  hipLaunchKernelGGL((reduce_kernel<SRC, VEC, kQuadsPerThread, INFL>), dim3(*blocks), dim3(kBlock), lds, s, a);
+hipError_t reduce_launch(const ReduceArgs& args, size_t lds, hipStream_t s, int* blocks) {
+  const int grid = stream_grid(args.n - args.head, kQuadsPerThread);
+  const ReduceArgs a = route_partials(args, grid, blocks);
+  hipLaunchKernelGGL((reduce_kernel<SRC, VEC, kQuadsPerThread, INFL>), dim3(grid), dim3(kBlock), lds, s, a);
   return hipGetLastError();
 }
 
@@ -871,9 +894,10 @@ int scan_grid(int64_t n) {
   return g < kScanGrid ? g : kScanGrid;
 }
 
-hipError_t launch_scan(const ReduceArgs& a, int src, hipStream_t s, int* blocks) {
-  *blocks = scan_grid(a.n);
-  const dim3 grid(*blocks);
+hipError_t launch_scan(const ReduceArgs& args, int src, hipStream_t s, int* blocks) {
+  const int g = scan_grid(args.n);
+  const ReduceArgs a = route_partials(args, g, blocks);
+  const dim3 grid(g);
   if (src == kSrcF16) hipLaunchKernelGGL(scan_kernel<kSrcF16>, grid, dim3(kBlock), 0, s, a);
   else if (src == kSrcBF16) hipLaunchKernelGGL(scan_kernel<kSrcBF16>, grid, dim3(kBlock), 0, s, a);
   else return hipErrorInvalidValue;

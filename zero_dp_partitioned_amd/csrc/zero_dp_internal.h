@@ -85,6 +85,9 @@ struct AdamArgs {
   double* partials;  // one per block (fused and optimistic pipelines); null in the checked one
   int64_t head;      // leading elements (0-3) block 0 updates one by one, so that the quad
                      // path starts where every array is aligned (see aligned_head)
+  double* level2 = nullptr;  // the group's level-2 partials: a launch of at most kFoldBlocks
+                             // blocks writes them directly instead of `partials` (no fold)
+  int32_t fill = 0;          // set by the launcher: partial slots [grid, fill) are written as 0
 };
 
 // Arguments of the average kernel (checked pipeline) and of the single-copy scan.
@@ -95,6 +98,8 @@ struct ReduceArgs {
   const zero_step_state* state;
   double* partials;
   int64_t head;    // as AdamArgs::head
+  double* level2 = nullptr;  // as AdamArgs::level2
+  int32_t fill = 0;          // as AdamArgs::fill
 };
 
 // Fold one launch's block partials into a group's level-2 partials, in a
@@ -183,8 +188,10 @@ inline int stream_grid(int64_t n, int quads = kQuadsPerThread) {
 }
 
 // Launchers (kernels.hip). Each returns the hipError_t of its launches.
-// `vec` selects the aligned quad path; *blocks receives the grid size, which is
-// the number of block partials the launch writes.
+// `vec` selects the aligned quad path; *blocks receives the number of block
+// partials the launch leaves to fold: its grid size, or 0 when it wrote the
+// group's level-2 partials itself (args.level2 set and a grid of at most
+// kFoldBlocks blocks).
 // batch_lds: dynamic LDS bytes per block of the batched schedule's launches,
 // which caps them at kBatchBlocksPerCU blocks per CU on the current device.
 hipError_t launch_adam(const AdamArgs& a, int src_kind, bool vec, int mode, size_t batch_lds, hipStream_t s,
