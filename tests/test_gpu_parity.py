@@ -155,6 +155,12 @@ FUSED_CASES = [
     (50_001, 2, "bf16", 0, 1, "table"),         # unaligned fp32 state: element path
     (4_500_001, 1, "bf16", 0, 0, "table"),      # 1,099 tiles (grid-stride rounds: test_grid_stride_rounds)
     (4_500_013, 3, "f16", 7, 0, "table"),
+    # either side of 256 blocks: up to 256 the launch writes the level-2 partials itself, past it a fold
+    (1_048_576, 1, "bf16", 0, 0, "table"),      # 256 tiles of 4096
+    (1_048_577, 1, "bf16", 0, 0, "table"),      # 257
+    (1_048_579, 4, "f16", 0, 1, "shift1"),      # 3-element head, then 256 tiles
+    (2_097_152, 32, "f16", 2, 0, "table"),      # 256 wide tiles of 8192
+    (2_097_153, 32, "bf16", 0, 0, "strided"),   # 257
 ]
 
 
@@ -199,7 +205,10 @@ def test_replica_table_beyond_64_must_be_strided():
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("n,n_d,dt,use_avg", [(50_001, 8, "f16", True), (4099, 3, "bf16", True),
-                                              (4099, 2, "f16", False), (7, 5, "f16", True)])
+                                              (4099, 2, "f16", False), (7, 5, "f16", True),
+                                              # the averaging pass and the scan either side of 256 blocks
+                                              (1_048_576, 8, "f16", True), (1_048_577, 8, "bf16", True),
+                                              (1_048_576, 1, "bf16", False), (1_048_577, 1, "f16", False)])
 def test_checked_pipeline_skip_and_scale(n, n_d, dt, use_avg):
     tag = f"checked n={n} n_d={n_d} {dt} avg={use_avg}"
     print(f"[case] {tag}", flush=True)
@@ -238,15 +247,21 @@ def test_checked_pipeline_skip_and_scale(n, n_d, dt, use_avg):
     assert_u16_equal(down16(flat)[off:off + n], og.param, tag + " param")
 
 
-@pytest.mark.parametrize("mis", [0, 1, 4])
-def test_checked_single_copy_prepass_two_groups(mis):
+@pytest.mark.parametrize("mis,sizes", [(0, (30_011, 513)), (1, (30_011, 513)), (4, (30_011, 513)),
+                                       # either side of 256 blocks (level-2 partials written directly / folded)
+                                       (0, (1_048_577, 1_048_576)), (1, (1_048_576, 1_048_577))])
+def test_checked_single_copy_prepass_two_groups(mis, sizes):
+    _prepass_two_groups(mis, sizes)
+
+
+def _prepass_two_groups(mis, sizes=(30_011, 513)):
     """N_d = 1, two groups, dynamic scale: the norm pass scans the gradients
     directly, then the update re-reads them. mis: the copies start that many
     elements into their buffers (0: 16-byte aligned, the wide-load scan; 4:
     8-byte, 1: 2-byte aligned, the streaming pass's quad and element paths)."""
     dt = "bf16"
     odt = ORACLE_DT[dt]
-    sizes, wds = (30_011, 513), (0.1, 0.0)
+    wds = (0.1, 0.0)
     pol = oracle.Policy(skip_on_overflow=True, growth_interval=1000)
     sc = zdp.policy(True)
     dev_groups, ogs, flats = [], [], []
@@ -439,7 +454,8 @@ def test_fused_pipeline_reports_no_clip():
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("n,n_d,dt,off,misalign", [(70_001, 8, "f16", 3, 0), (4099, 1, "bf16", 0, 0),
-                                                   (30_000, 2, "f16", 8, 1), (40_961, 32, "bf16", 5, 0)])
+                                                   (30_000, 2, "f16", 8, 1), (40_961, 32, "bf16", 5, 0),
+                                                   (1_048_576, 8, "f16", 0, 0), (1_048_577, 2, "bf16", 4, 0)])
 def test_optimistic_pipeline(n, n_d, dt, off, misalign):
     tag = f"optimistic n={n} n_d={n_d} {dt} off={off} mis={misalign}"
     print(f"[case] {tag}", flush=True)
@@ -663,8 +679,8 @@ GRID_ROUND_CASES = {
     # averaging pass + norm + checked update, with two overflowing calls
     "checked n_d=8": lambda: test_checked_pipeline_skip_and_scale(50_001, 8, "f16", True),
     # the single-copy scan (16-byte aligned) and the streaming pre-pass (2-byte aligned)
-    "scan aligned": lambda: test_checked_single_copy_prepass_two_groups(0),
-    "scan unaligned": lambda: test_checked_single_copy_prepass_two_groups(1),
+    "scan aligned": lambda: _prepass_two_groups(0),
+    "scan unaligned": lambda: _prepass_two_groups(1),
     # optimistic update with overflowing calls: the restore kernel's loop
     "optimistic": lambda: test_optimistic_pipeline(70_001, 8, "f16", 3, 0),
     # clipped optimistic steps: the second pass's loop
