@@ -6,7 +6,11 @@ table, equally spaced buffer, packed unaligned, or each copy as far past
 alignment as the fp32 state, which the kernels peel as a short head), a pipeline (fused, checked,
 optimistic) with or without clipping, a loss scale, an inf or NaN written
 into a copy now and then, and the parameter vector's dtype (the gradients'
-most of the time, the other 16-bit type, or no fused writeback at all). The bar
+most of the time, the other 16-bit type, or no fused writeback at all). About
+half of the cases also cap every launch's grid (zdp.set_grid_limit) at a few
+blocks or just either side of 256 (on the small shards only the caps of a few
+blocks bind), so that blocks loop over tiles and launches write their level-2
+norm partials themselves or leave them to a fold. The bar
 is test_gpu_parity's: bit for bit, unless the two sides' clip multipliers are
 one ulp apart (then the stated tolerances from that call on)."""
 import numpy as np
@@ -52,21 +56,36 @@ def _case(seed, large=False):
     return dt, pipeline, clip, groups, scale, max_norm, inject, pdt
 
 
+def _grid_limit(seed, large=False):
+    """The case's block cap (0: none), drawn from a stream of its own so that
+    the case's other draws are unchanged."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7, int(large)])))
+    return int(rng.choice([0, 0, 0, 0, 0, 0, 0, 1, 2, 3, 7, 255, 256, 257]))
+
+
 @pytest.mark.parametrize("seed", range(N_CASES))
 def test_random_configuration(seed):
-    run_case(seed, _case(seed))
+    run_case(seed, _case(seed), _grid_limit(seed))
 
 
 @pytest.mark.parametrize("seed", range(N_LARGE))
 def test_random_large_configuration(seed):
-    run_case(seed, _case(seed, large=True))
+    run_case(seed, _case(seed, large=True), _grid_limit(seed, large=True))
 
 
-def run_case(seed, case):
+def run_case(seed, case, grid_limit=0):
+    zdp.set_grid_limit(grid_limit)
+    try:
+        _run_case(seed, case, grid_limit)
+    finally:
+        zdp.set_grid_limit(0)
+
+
+def _run_case(seed, case, grid_limit):
     dt, pipeline, clip, specs, scale, max_norm, inject, pdt = case
     dynamic = pipeline != "fused" and (pipeline == "optimistic" or seed % 2 == 0)
     tag = (f"seed {seed}: {dt} params {pdt} {pipeline} dynamic={dynamic} clip={max_norm:.3g} scale={scale} "
-           f"groups={specs}")
+           f"grid limit {grid_limit} groups={specs}")
     print(f"[case] {tag}", flush=True)
     odt = ORACLE_DT[dt]
     opdt = ORACLE_DT[pdt] if pdt else odt
