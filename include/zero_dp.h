@@ -109,7 +109,7 @@ typedef struct {
  *   after growth_interval applied steps in a row, S <- S * growth
  *   (growth_interval 0 = never).
  * max_grad_norm > 0: clip the unscaled gradient to this global norm
- *   [DeepSpeed walkthrough §6 step 3 "unscale and clip"]: multiplier
+ *   [DeepSpeed walkthrough §6 step 3, unscaling and clipping]: multiplier
  *   c = min(1, max_norm / (norm + 1e-6)) formed in fp64 and rounded once to
  *   fp32, g <- (avg * (1/S)) * c; 0 = no clipping.
  * optimistic = 1 (with skip_on_overflow = 1): instead of waiting for the

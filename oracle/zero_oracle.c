@@ -160,7 +160,7 @@ static uint16_t encode16(int dt, float x)
 /* ------------------------------------------------------------------------- */
 /* Partition [DS12 §4 ②]: base = numel / N_d, rem = numel % N_d; the first    */
 /* rem ranks get one element more. Optional padding of the flat length to a   */
-/* multiple of align_elems [DS12 §4 ① and §7 "对齐 padding"].                 */
+/* multiple of align_elems [DS12 §4 ① and §7, alignment padding].           */
 /* ------------------------------------------------------------------------- */
 
 int oracle_partition(int64_t numel, int32_t n_d, int64_t align_elems,
