@@ -162,3 +162,22 @@ def _run_case(seed, case, grid_limit):
             bar.param16(got[off:off + n], og.param, f"{tag} call {k + 1} group {gi} param")
             outside = np.r_[0:off, off + n:flats0[gi].size]
             assert_u16_equal(got[outside], flats0[gi][outside], f"{tag} group {gi} outside the slice")
+
+
+@pytest.mark.parametrize("pipeline", ["fused", "checked", "optimistic"])
+def test_the_maximum_number_of_groups(pipeline):
+    """ZERO_MAX_GROUPS (8) groups in one step, of assorted lengths, copy
+    counts, layouts and decays: one shared norm and verdict, eight sets of β
+    powers, every level-2 slot of the workspace. The second call carries an
+    inf in group 0 (voided under the dynamic scale of the checked and
+    optimistic pipelines, which also clip)."""
+    assert zdp.MAX_GROUPS == 8
+    shapes = [(1, 1, "table", 0, 0.0), (4097, 2, "strided", 3, 0.1), (30_011, 3, "packed", 1, 0.1),
+              (7, 4, "table", 5, 0.0), (300_001, 8, "shift", 2, 0.1), (255, 1, "table", 8, 0.0),
+              (65_536, 32, "table", 0, 0.1), (2, 5, "strided", 7, 0.0)]
+    specs = [dict(n=n, n_d=nd, layout=lay, off=off, mis=1 if lay == "shift" else 0, wd=wd)
+             for n, nd, lay, off, wd in shapes]
+    total = sum(g["n"] / g["n_d"] for g in specs)
+    max_norm = 1e-3 * np.sqrt(total) * 0.8 if pipeline != "fused" else 0.0
+    case = ("bf16", pipeline, pipeline != "fused", specs, 1024.0, max_norm, [False, True, False], "bf16")
+    run_case(2 * 4321, case)   # an even seed: the checked pipeline takes the dynamic scale
