@@ -496,6 +496,61 @@ def test_optimistic_pipeline(n, n_d, dt, off, misalign):
     assert ost.step == 5
 
 
+@pytest.mark.parametrize("pipeline", ["fused", "checked", "optimistic"])
+def test_zero_gradients(pipeline):
+    """A step on gradients that are all zero (some -0): norm 0, no flag, the
+    clip multiplier 1 (a threshold is set in the dynamic pipelines), m and v
+    stay 0 and only the decoupled decay moves the master; then a call with
+    ordinary gradients. Every element and the state against the oracle."""
+    n, n_d, dt, off = 50_001, 4, "bf16", 3
+    tag = f"zero gradients {pipeline}"
+    print(f"[case] {tag}", flush=True)
+    odt = ORACLE_DT[dt]
+    dynamic = pipeline != "fused"
+    pol = oracle.Policy(skip_on_overflow=dynamic, max_grad_norm=0.5 if dynamic else 0.0)
+    sc = zdp.policy(True, max_grad_norm=0.5, optimistic=pipeline == "optimistic") if dynamic else None
+    master0 = normal_f32_np(n, 0.02, (16, "master"))
+    flat0 = to16_bits_np(normal_f32_np(n + off + 2, 0.02, (16, "flat")), dt)
+    flat0[off:off + n] = to16_bits_np(master0, dt)
+    alt = {}
+    if pipeline == "optimistic":
+        alt = dict(master_alt=torch.zeros(n, device=DEV), exp_avg_alt=torch.zeros(n, device=DEV),
+                   exp_avg_sq_alt=torch.zeros(n, device=DEV))
+    grp = zdp.Group(up32(master0), torch.zeros(n, device=DEV), torch.zeros(n, device=DEV),
+                    flat_param=up16(flat0, dt), param_offset=off, weight_decay=0.1, **alt)
+    ws, st = zdp.new_workspace(1), zdp.new_state(1024.0)
+    avg = torch.empty(n, device=DEV)
+    og = oracle.Group(replicas=None, grad_dt=odt, master=master0.copy(), m=np.zeros(n, np.float32),
+                      v=np.zeros(n, np.float32), param=flat0[off:off + n].copy(), param_dt=odt, weight_decay=0.1)
+    ost = oracle.State(loss_scale=1024.0)
+    for k in range(2):
+        if k == 0:
+            reps = [np.zeros(n, np.uint16) for _ in range(n_d)]
+            reps[1][::3] = 0x8000   # -0
+        else:
+            reps = [grads16_np(n, dt, ost.loss_scale, (16, "g", r)) for r in range(n_d)]
+        dreps = [up16(r, dt) for r in reps]
+        if pipeline == "checked":
+            zdp.reduce_grad_segment(dreps, avg, ws, 0, st)
+            zdp.grad_norm_overflow(None, ws, 1, st, sc)
+            grp.replicas, grp.avg = None, avg
+        else:
+            grp.replicas, grp.avg = dreps, None
+        zdp.adam_step([grp], ws, st, sc)
+        og.replicas = reps
+        oracle.step([og], pol, ost)
+        torch.cuda.synchronize()
+        s = _compare_state(f"{tag} call {k + 1}", st, ost)
+        if k == 0:
+            assert s["grad_norm_sq"] == 0.0 and s["overflow"] == 0 and s["clip_coef"] == 1.0, (tag, s)
+        cm, cmm, cv = zdp.current_state(grp, s)
+        _compare_group(f"{tag} call {k + 1}", cm, cmm, cv, og)
+        if k == 0:
+            assert not torch.any(cmm != 0) and not torch.any(cv != 0), tag
+        assert_u16_equal(down16(grp.flat_param)[off:off + n], og.param, f"{tag} call {k + 1} param")
+    assert ost.step == 2
+
+
 # --------------------------------------------------------------------------
 # limits and concurrency
 # --------------------------------------------------------------------------
