@@ -551,6 +551,59 @@ def test_zero_gradients(pipeline):
     assert ost.step == 2
 
 
+@pytest.mark.parametrize("pipeline", ["checked", "optimistic"])
+def test_loss_scale_floor_and_growth(pipeline):
+    """The scale's bookkeeping at its limits: from 1.0 with a floor of 0.25,
+    three overflowing calls in a row halve it to 0.5 and 0.25 and then leave
+    it at the floor; with a growth window of one applied step and a factor of
+    4, the next calls multiply it each time. Every element and the state
+    against the oracle."""
+    n, n_d, dt = 20_003, 2, "f16"
+    tag = f"scale floor/growth {pipeline}"
+    print(f"[case] {tag}", flush=True)
+    odt = ORACLE_DT[dt]
+    pol = oracle.Policy(skip_on_overflow=True, growth_interval=1, backoff=0.5, growth=4.0, min_scale=0.25)
+    sc = zdp.policy(True, growth_interval=1, backoff=0.5, growth=4.0, min_scale=0.25,
+                    optimistic=pipeline == "optimistic")
+    master0 = normal_f32_np(n, 0.02, (17, "master"))
+    flat0 = to16_bits_np(master0, dt)
+    alt = {}
+    if pipeline == "optimistic":
+        alt = dict(master_alt=torch.zeros(n, device=DEV), exp_avg_alt=torch.zeros(n, device=DEV),
+                   exp_avg_sq_alt=torch.zeros(n, device=DEV))
+    grp = zdp.Group(up32(master0), torch.zeros(n, device=DEV), torch.zeros(n, device=DEV),
+                    flat_param=up16(flat0, dt), **alt)
+    ws, st = zdp.new_workspace(1), zdp.new_state(1.0)
+    avg = torch.empty(n, device=DEV)
+    og = oracle.Group(replicas=None, grad_dt=odt, master=master0.copy(), m=np.zeros(n, np.float32),
+                      v=np.zeros(n, np.float32), param=flat0.copy(), param_dt=odt)
+    ost = oracle.State(loss_scale=1.0)
+    scales = []
+    for k in range(6):
+        reps = [grads16_np(n, dt, ost.loss_scale, (17, "g", k, r)) for r in range(n_d)]
+        if k < 3:
+            reps[0] = reps[0].copy()
+            reps[0][(k * 977) % n] = POS_INF[dt]
+        dreps = [up16(r, dt) for r in reps]
+        if pipeline == "checked":
+            zdp.reduce_grad_segment(dreps, avg, ws, 0, st)
+            zdp.grad_norm_overflow(None, ws, 1, st, sc)
+            grp.replicas, grp.avg = None, avg
+        else:
+            grp.replicas, grp.avg = dreps, None
+        zdp.adam_step([grp], ws, st, sc)
+        og.replicas = reps
+        oracle.step([og], pol, ost)
+        torch.cuda.synchronize()
+        s = _compare_state(f"{tag} call {k + 1}", st, ost)
+        scales.append(s["loss_scale"])
+        cm, cmm, cv = zdp.current_state(grp, s)
+        _compare_group(f"{tag} call {k + 1}", cm, cmm, cv, og)
+        assert_u16_equal(down16(grp.flat_param), og.param, f"{tag} call {k + 1} param")
+    assert scales == [0.5, 0.25, 0.25, 1.0, 4.0, 16.0], scales
+    assert ost.step == 3
+
+
 # --------------------------------------------------------------------------
 # limits and concurrency
 # --------------------------------------------------------------------------
