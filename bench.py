@@ -96,6 +96,56 @@ def copy_calibration(args):
     print(json.dumps({"copy_calibration_bytes": args.copy_calibration, "launches": args.steps}), flush=True)
 
 
+COPY_BYTES = 2 << 30
+
+
+def copy_ceiling(setup, reps=10):
+    """The bandwidth (bytes read + bytes written per second) of the library's
+    two-stream copy probe in the step's own arena: src0 -> dst0 and src1 ->
+    dst1 from unused ranges, each stream from one HBM region into the other
+    where the arena has two, so that each region serves one read and one
+    write stream as in a step of half reads, half writes. None if the arena
+    has no room."""
+    import torch
+
+    import zero_dp_partitioned_amd as zdp
+    if setup.arena is None:
+        return None
+    A = zdp.ARENA_ALIGN
+    spans = []   # (offset, region) of COPY_BYTES-sized pieces of the free ranges
+    for off, nb in setup.free:
+        o = (off + A - 1) // A * A
+        while o + COPY_BYTES <= off + nb:
+            spans.append((o, o // zdp.HBM_REGION_BYTES))
+            o += COPY_BYTES
+    if len(spans) < 4:
+        return None
+    by = {}
+    for sp in spans:
+        by.setdefault(sp[1], []).append(sp)
+    regs = sorted(by, key=lambda r: -len(by[r]))
+    if len(regs) >= 2 and len(by[regs[0]]) >= 2 and len(by[regs[1]]) >= 2:
+        (s0, d1), (d0, s1) = by[regs[0]][:2], by[regs[1]][:2]
+    else:
+        s0, s1, d0, d1 = spans[:4]
+    view = [zdp.arena_view(setup.arena, sp[0], COPY_BYTES, torch.uint8) for sp in (s0, s1, d0, d1)]
+    zdp.copy_probe(*view)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        zdp.copy_probe(*view)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    moved = 4 * COPY_BYTES
+    return {"gbps": moved / (ms / 1e3) / 1e9, "bytes": moved,
+            "what": f"zero_copy_probe: two {COPY_BYTES >> 30} GiB streams in unused ranges of the step's arena "
+                    f"(region {s0[1]} -> {d0[1]} and {s1[1]} -> {d1[1]}), bytes read + written per second, mean "
+                    f"of {reps} launches"}
+
+
 def log(args, *a):
     if not args.quiet:
         print("[bench]", *a, file=sys.stderr, flush=True)
@@ -134,6 +184,7 @@ class Setup:
         specs = layout.step_specs(shards, wl.n_d, torch_dtype(wl.grad_dt), torch_dtype(wl.param_dt),
                                   spec_pipeline, table)
         buf, self.placement = layout.allocate(specs, dev, placement, whole=whole, n_regions=n_regions)
+        self.arena, self.free = buf.get("arena"), buf.get("free", [])   # for the copy ceiling
         for gi, (spec, (psi, off, n)) in enumerate(zip(wl.groups, shards)):
             master = buf[(gi, "master")][:n]
             fill_normal_(master, 0.02, derive_seed(wl.key, gi, "master"))
@@ -337,6 +388,10 @@ def main():
         rec = json.load(open(TRAFFIC_FILE)).get(key)
         if rec and rec.get("kernel_source") == kernel_source_hash():
             traffic = rec.get("bytes_per_step")
+    ceiling = copy_ceiling(setup)
+    if ceiling:
+        ceiling["achieved_frac"] = achieved / ceiling["gbps"]
+        log(args, f"copy ceiling {ceiling['gbps']:.0f} GB/s; the step reaches {ceiling['achieved_frac']:.3f} of it")
     cpu = None
     if args.cpu_sample > 0:
         cpu = cpu_baseline(setup, args.cpu_sample, args.cpu_single, args)
@@ -365,6 +420,7 @@ def main():
                      "kernel": STEP_KERNELS[pipeline] + ", HIP events around each step",
                      "kernel_ms": ev_mean, "algorithmic_bytes": algo_bytes},
         "cpu_baseline": cpu,
+        "copy_ceiling": ceiling,
     }
     print(json.dumps(out), flush=True)
 

@@ -358,6 +358,20 @@ int zero_cast_writeback(const float* master, int64_t n, void* flat_param, int64_
  * Errors: INVALID_ARG for max_blocks < 0. */
 int zero_set_grid_limit(int32_t max_blocks);
 
+/* ---- measurement ----------------------------------------------------------
+ * Not an operation of the pages. Copies n_bytes from src0 to dst0 and from
+ * src1 to dst1 (device buffers, 16-byte aligned, n_bytes a multiple of 16;
+ * the ranges must not overlap) with the update kernel's access shape: one
+ * block per 16 KiB tile of each stream, 16-byte non-temporal loads and
+ * stores, each wavefront access one contiguous 1 KiB run. A step of half
+ * reads, half writes over buffers in two HBM regions (N_d = 1) moves its bytes
+ * the way this copy does with src0/dst1 in one region and src1/dst0 in the
+ * other, so its bandwidth is the ceiling such a step meets on that placement;
+ * bench.py reports it beside the step. Stream-ordered, allocates nothing.
+ * Errors: INVALID_ARG (negative or unaligned size, NULL buffer), ALIGNMENT,
+ * UNSUPPORTED (not gfx950), HIP. */
+int zero_copy_probe(const void* src0, const void* src1, void* dst0, void* dst1, int64_t n_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

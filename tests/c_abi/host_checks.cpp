@@ -149,6 +149,12 @@ static void device_call_checks() {
   EXPECT(zdp::stream_grid(int64_t(1) << 40) == 3 && zdp::stream_grid(10) == 1);
   EXPECT(zero_set_grid_limit(0) == ZERO_OK);
   EXPECT(zdp::stream_grid(int64_t(1) << 40) == zdp::kMaxGrid && zdp::stream_grid(4097) == 2);
+  // the copy probe's argument checks
+  EXPECT(zero_copy_probe(fake, fake, fake, fake, -16, nullptr) == ZERO_ERR_INVALID_ARG);
+  EXPECT(zero_copy_probe(fake, fake, fake, fake, 17, nullptr) == ZERO_ERR_INVALID_ARG);
+  EXPECT(zero_copy_probe(fake, fake, fake, nullptr, 32, nullptr) == ZERO_ERR_INVALID_ARG);
+  EXPECT(zero_copy_probe(fake, (void*)0x100008, fake, fake, 32, nullptr) == ZERO_ERR_ALIGNMENT);
+  EXPECT(zero_copy_probe(nullptr, nullptr, nullptr, nullptr, 0, nullptr) == ZERO_OK);  // nothing to copy
 }
 
 // Which launches take the batched schedule (update) and the batched read

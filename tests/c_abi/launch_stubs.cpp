@@ -25,5 +25,6 @@ hipError_t launch_state_init(zero_step_state*, float, hipStream_t) { return neve
 hipError_t launch_cast(const CastArgs&, bool, hipStream_t) { return never("cast"); }
 hipError_t launch_restore(const RestoreArgs&, bool, hipStream_t) { return never("restore"); }
 hipError_t static_scratch(void**) { return never("static scratch"); }
+hipError_t launch_copy_probe(const void*, const void*, void*, void*, int64_t, hipStream_t) { return never("copy probe"); }
 
 }  // namespace zdp

@@ -72,6 +72,11 @@ def test_json_line_has_the_contract_fields(args):
     assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-12
     assert rf["traffic"] is None or rf["traffic"] > 0
+    cc = d["copy_ceiling"]   # a plain copy in the step's arena; none when the arena has no room (tiny)
+    if "13b_nd8" in args:
+        assert cc["gbps"] > 1000 and abs(cc["achieved_frac"] - rf["achieved"] / cc["gbps"]) < 1e-12
+    else:
+        assert cc is None
     cpu = d["cpu_baseline"]
     if "--cpu-sample" in args and args[args.index("--cpu-sample") + 1] != "0":
         assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["unit"] == "params/s"

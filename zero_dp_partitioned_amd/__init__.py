@@ -29,7 +29,7 @@ ARENA_ALIGN = 2 << 20
 EXPORTS = ("zero_partition", "zero_partition_tensors", "zero_workspace_bytes",
            "zero_last_error", "zero_state_init", "zero_reduce_grad_segment",
            "zero_grad_norm_overflow", "zero_adam_step", "zero_cast_writeback", "zero_plan_arena",
-           "zero_set_grid_limit", "zero_adam_step_static")
+           "zero_set_grid_limit", "zero_adam_step_static", "zero_copy_probe")
 
 
 class ZeroError(RuntimeError):
@@ -124,6 +124,7 @@ def load():
         L.zero_plan_arena.argtypes = [ctypes.POINTER(ArenaBuffer), i32, i64, i32, i64, ctypes.POINTER(i64)]
         L.zero_set_grid_limit.argtypes = [i32]
         L.zero_adam_step_static.argtypes = [ctypes.POINTER(_Group), i32, ctypes.POINTER(Policy), vp, vp]
+        L.zero_copy_probe.argtypes = [vp, vp, vp, vp, i64, vp]
         for name in EXPORTS:
             fn = getattr(L, name)
             if name not in ("zero_workspace_bytes", "zero_last_error"):
@@ -168,6 +169,21 @@ def partition_tensors(numels, n_d, rank, align_elems=1):
 def set_grid_limit(max_blocks):
     """Cap the blocks of every streaming launch (0: no cap); for tests."""
     _check(load().zero_set_grid_limit(int(max_blocks)))
+
+
+def copy_probe(src0, src1, dst0, dst1, stream=None):
+    """Copy src0 -> dst0 and src1 -> dst1 (uint8 device tensors of one size,
+    a multiple of 16 bytes) with the update kernel's access shape: the
+    bandwidth reference for a step of half reads, half writes."""
+    torch = _torch()
+    dev = src0.device if isinstance(src0, torch.Tensor) else None
+    nb = _nbytes(src0) if isinstance(src0, torch.Tensor) else 0
+    if dev is None or dev.type != "cuda":
+        raise ValueError("copy_probe: src0 must be a device tensor")
+    for name, t in (("src0", src0), ("src1", src1), ("dst0", dst0), ("dst1", dst1)):
+        _need(t, name, (torch.uint8,), dev, nb, exact=True)
+    _check(load().zero_copy_probe(_ptr(src0), _ptr(src1), _ptr(dst0), _ptr(dst1), ctypes.c_int64(nb),
+                                  _stream(stream)))
 
 
 def workspace_bytes(n_groups):

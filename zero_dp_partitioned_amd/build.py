@@ -19,7 +19,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "inclu
 DEVICE = [f"--offload-arch={ARCH}", "-ffp-contract=off", "-fno-fast-math",
           "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-SOURCES = [("api.cpp", False), ("kernels.hip", True), ("static_scratch.hip", True)]
+SOURCES = [("api.cpp", False), ("kernels.hip", True), ("static_scratch.hip", True), ("copy_probe.hip", True)]
 
 
 def hipcc():

@@ -16,6 +16,9 @@ using namespace zdp;
 
 namespace zdp {
 std::atomic<int32_t> g_grid_limit{0};
+// Two-stream copy of `words` 16-byte words, src0 -> dst0 and src1 -> dst1 (copy_probe.hip).
+hipError_t launch_copy_probe(const void* src0, const void* src1, void* dst0, void* dst1, int64_t words,
+                             hipStream_t s);
 }  // namespace zdp
 
 namespace {
@@ -625,6 +628,18 @@ int zero_set_grid_limit(int32_t max_blocks) {
   if (max_blocks < 0) return fail(ZERO_ERR_INVALID_ARG, "max_blocks = %d < 0", max_blocks);
   g_grid_limit.store(max_blocks, std::memory_order_relaxed);
   return ZERO_OK;
+}
+
+int zero_copy_probe(const void* src0, const void* src1, void* dst0, void* dst1, int64_t n_bytes, void* stream) {
+  if (n_bytes < 0) return fail(ZERO_ERR_INVALID_ARG, "n_bytes < 0");
+  if (n_bytes % 16) return fail(ZERO_ERR_INVALID_ARG, "n_bytes = %lld is not a multiple of 16", (long long)n_bytes);
+  if (n_bytes == 0) return ZERO_OK;
+  if (!src0 || !src1 || !dst0 || !dst1) return fail(ZERO_ERR_INVALID_ARG, "a buffer is NULL");
+  if (!aligned(src0, 16) || !aligned(src1, 16) || !aligned(dst0, 16) || !aligned(dst1, 16))
+    return fail(ZERO_ERR_ALIGNMENT, "buffers must be 16-byte aligned");
+  if (int rc = check_device()) return rc;
+  hipError_t e = launch_copy_probe(src0, src1, dst0, dst1, n_bytes / 16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ZERO_OK : hip_fail(e, "copy probe launch");
 }
 
 int zero_cast_writeback(const float* master, int64_t n, void* flat_param, int64_t offset, int32_t param_dt,
