@@ -60,6 +60,14 @@ MUTATIONS = [
     ("clip allowed to scale up", "return (float)(c < 1.0 ? c : 1.0);", "return (float)c;"),
     ("shard norm ignored for a sample", "            norm2 = given_norm2;\n", ""),
     ("shard flag ignored for a sample", "            flag = given_flag;\n", ""),
+    ("scale floor ignored", "        if (s < policy->min_scale)\n            s = policy->min_scale;\n", ""),
+    ("growth ignores its window", "st->good_steps == policy->growth_interval) {", "st->good_steps >= 1) {"),
+    ("clip guard dropped", "double c = max_norm / (sqrt(norm2) + 1e-6);", "double c = max_norm / sqrt(norm2);"),
+    ("padding one unit too far", "padded = numel + (align_elems - r);",
+     "padded = numel + (align_elems - r) + align_elems;"),
+    ("skip keeps the growth window", "        st->good_steps = 0;\n        st->skipped = 1;\n",
+     "        st->skipped = 1;\n"),
+    ("fp16 NaN not canonical", "return 0x7e00; /* canonical quiet NaN */", "return sign | 0x7e01;"),
 ]
 
 
