@@ -68,6 +68,15 @@ MUTATIONS = [
     ("skip keeps the growth window", "        st->good_steps = 0;\n        st->skipped = 1;\n",
      "        st->skipped = 1;\n"),
     ("fp16 NaN not canonical", "return 0x7e00; /* canonical quiet NaN */", "return sign | 0x7e01;"),
+    ("bf16 decode shifted by 15", "uint32_t bits = (uint32_t)h << 16;", "uint32_t bits = (uint32_t)h << 15;"),
+    ("decay after the update", "        float next = theta - lrf * upd;\n",
+     "        float next = (theta - lrf * upd) * (weight_decay != 0.0 ? decay : 1.0f);\n"),
+    ("decay without the learning rate", "const float decay = (float)(1.0 - lr * weight_decay);",
+     "const float decay = (float)(1.0 - weight_decay);"),
+    ("clip multiplier squared", "        g = g * clip;                            /* clip (1 = none) */\n",
+     "        g = g * (clip < 1.0f ? clip * clip : 1.0f);\n"),
+    ("parameter written from the pre-update master", "            param[j] = encode16(param_dt, next);",
+     "            param[j] = encode16(param_dt, theta);"),
 ]
 
 
