@@ -324,7 +324,8 @@ int zero_adam_step(const zero_group* groups, int32_t n_groups, const zero_policy
  * partials in a static device array of the library (16 MiB + 16 KiB,
  * ZERO_MAX_GROUPS groups, any shard size) instead of a caller's workspace.
  * Each GPU the library runs on holds one copy of that array until the process
- * ends; its address is looked up on the first call on a device. The call
+ * ends; its address is looked up on the first call on a device (code that
+ * captures the call into a graph makes one call on the device first). The call
  * allocates and frees nothing. Every call on a GPU shares that GPU's array,
  * so calls that overlap on one GPU (concurrent streams, threads) race; order
  * them. The contents need no initialisation (each call writes the partials it

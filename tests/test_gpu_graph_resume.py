@@ -66,6 +66,56 @@ def test_graph_capture_and_replay_matches_eager():
 
 
 @pytest.mark.parametrize("optimistic", [False, True])
+def test_static_step_captured_in_a_graph(optimistic):
+    """zero_adam_step_static, the entry point for callers that cannot
+    allocate, captured once and replayed: every replay gives the bits of the
+    eager zero_adam_step with a workspace (an overflowing call voids a step
+    of the optimistic pipeline, whose restore launch is in the graph). The
+    first call on the device, which looks the static array up, is made before
+    the capture."""
+    n, n_d, steps = 300_001, 4, 4
+    eager, graphed = _setup(n, n_d, 22), _setup(n, n_d, 22)
+    pol = zdp.policy(True, optimistic=True, growth_interval=2) if optimistic else None
+    if optimistic:
+        for g in (eager, graphed):
+            g.master_alt, g.exp_avg_alt, g.exp_avg_sq_alt = (torch.zeros(n, device=DEV) for _ in range(3))
+    ws_e, st_e = zdp.new_workspace(1), zdp.new_state(1024.0 if optimistic else 1.0)
+    st_g = zdp.new_state(1024.0 if optimistic else 1.0)
+    # the first call on the device, outside the capture
+    tiny = _setup(4099, 1, 23)
+    zdp.adam_step_static([tiny], zdp.new_state(1.0))
+    _load_grads(graphed, 0, 22)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        zdp.adam_step_static([graphed], st_g, pol)
+    torch.cuda.synchronize()
+    assert zdp.read_state(st_g)["step"] == 0
+    for k in range(steps):
+        scale = zdp.read_state(st_e)["loss_scale"]
+        for g in (eager, graphed):
+            _load_grads(g, k, 22, scale)
+            if optimistic and k == 1:
+                g.replicas[2][n // 3] = float("inf")
+        zdp.adam_step([eager], ws_e, st_e, pol)
+        graph.replay()
+        junk = torch.randn(1000, device=DEV).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        assert float(junk) == float(junk)
+        tag = f"replay {k + 1}"
+        se, sg = zdp.read_state(st_e), zdp.read_state(st_g)
+        for x, y, name in zip(zdp.current_state(graphed, sg), zdp.current_state(eager, se),
+                              ("master", "exp_avg", "exp_avg_sq")):
+            assert_bits_equal(down32(x), down32(y), f"{tag} {name}")
+        assert_u16_equal(down16(graphed.flat_param), down16(eager.flat_param), tag + " param")
+        np.testing.assert_array_equal(st_g.cpu().numpy(), st_e.cpu().numpy())
+    se = zdp.read_state(st_e)
+    assert se["step"] == (steps - 1 if optimistic else steps)
+
+
+@pytest.mark.parametrize("optimistic", [False, True])
 def test_checkpoint_resume_is_bit_identical(optimistic):
     n, n_d, steps, cut = 200_003, 2, 6, 3
     pol = zdp.policy(True, growth_interval=2, optimistic=optimistic)
