@@ -335,15 +335,17 @@ def test_fused_two_groups_adamw():
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
-@pytest.mark.parametrize("off", [0, 1, 2, 4, 8, 13])
-def test_cast_writeback(dt, off):
+@pytest.mark.parametrize("off,mis", [(0, 0), (1, 0), (2, 0), (4, 0), (8, 0), (13, 0), (0, 1), (5, 3)])
+def test_cast_writeback(dt, off, mis):
+    """mis: the fp32 master starts that many elements past a 16-byte boundary."""
     rng = np.random.Generator(np.random.PCG64(10 + off))
     n = 20_003
     x = (rng.standard_normal(n) * 10.0 ** rng.uniform(-10, 6, n)).astype(np.float32)
     x[:12] = [np.nan, -np.nan, np.inf, -np.inf, 0.0, -0.0, 65504.0, 65520.0, 3.4e38, 1e-40, -1e-45, 2.0 ** -24]
     flat0 = np.arange(n + off + 3, dtype=np.uint16)
     flat = up16(flat0, dt)
-    zdp.cast_writeback(up32(x), flat, off)
+    master = carve(n + 8, mis, n, torch.float32).copy_(up32(x))
+    zdp.cast_writeback(master, flat, off)
     got = down16(flat)
     assert_u16_equal(got[off:off + n], oracle.encode16(x, ORACLE_DT[dt]), f"cast {dt} off={off}")
     assert_u16_equal(got[:off], flat0[:off], "before")
@@ -798,7 +800,7 @@ GRID_ROUND_CASES = {
     "checked clip": lambda: test_checked_pipeline_with_clipping(60_001, 4, "f16", False, 0.02, 1.0),
     # standalone average and cast
     "average": lambda: test_reduce_grad_segment(8, "f16", "shift2"),
-    "cast": lambda: test_cast_writeback("bf16", 1),
+    "cast": lambda: test_cast_writeback("bf16", 1, 0),
 }
 
 
